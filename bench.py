@@ -1,0 +1,281 @@
+"""Benchmark of the THD layout-transform hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gdn128k]
+
+One step is one pass of the whole hot path over one micro-batch already
+resident in HBM: build the route from the padded boundaries, swap the
+activations zigzag -> contiguous and back (layers x 2 swaps), and write the
+document-aware label shift / MTP roll / valid mask.  The default workload is
+the GDN-style 128K batch (cp 4, T = 131072, rows [T, 16, 128] bf16).
+
+Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes (every
+swap reads and writes each row once; the roll reads the ids and writes its
+streams and masks) divided by the step time, in GB/s.  ``roofline`` prices the
+swap kernel (the dominant kernel) against the MI355X HBM peak; its duration is
+the mean of HIP events recorded around every swap launch in the timed region,
+on the stream the kernel runs on.  ``cpu_baseline`` times the CPU oracle on
+the host over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="gdn128k")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def step_bytes(w, layers):
+    swap = 2 * w.total * w.row_bytes
+    roll = 0
+    if w.max_shift:
+        j = w.max_shift
+        roll = 8 * w.total + 8 * j * w.total + (j + 1) * w.total
+    return swap, roll, 2 * layers * swap + roll
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def oracle_baseline(w, layers, budget_s):
+    """The CPU oracle as it stands: per-token route, np.take swaps, per-slot roll."""
+    import numpy as np
+
+    import oracle
+
+    x = w.rows_host()
+    ids = w.ids()
+    cu = w.cu_padded
+    _, _, total_bytes = step_bytes(w, layers)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        oracle.build_route(cu.tolist(), w.cp, w.total)
+        cur = x
+        for _ in range(layers):
+            a = oracle.swap_rows(cur, cu, w.cp, w.total, "z2c")
+            cur = oracle.swap_rows(a, cu, w.cp, w.total, "c2z")
+        if w.max_shift:
+            oracle.roll_labels(ids, cu, w.cu_real, w.total, w.max_shift, 0)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 50:
+            break
+    assert np.array_equal(cur, x)
+    return {
+        "value": round(total_bytes * steps / el / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{steps} full step(s) of the {w.name} workload ({layers} layer(s)), {el:.1f} s; "
+                  f"single-threaded NumPy on 1 of {os.cpu_count()} host threads ({cpu_model()})",
+        "ms_per_step": round(el / steps * 1e3, 1),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the cross-rank exchange is "
+              "emulated as one global permutation on a single device; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import context_packed_sequence_amd as thd
+    import workloads
+
+    w = workloads.make(args.workload)
+    layers = w.layers
+    total, cp = w.total, w.cp
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    cu = torch.from_numpy(w.cu_padded).to(dev)
+    cu_real = torch.from_numpy(w.cu_real).to(dev)
+    ids = torch.from_numpy(w.ids()).to(dev)
+    g = torch.Generator(device=dev).manual_seed(workloads.BASE_SEED + w.index)
+    x = torch.randn((total,) + tuple(w.row_shape), dtype=torch.bfloat16, device=dev, generator=g)
+    a = torch.empty_like(x)
+    b = torch.empty_like(x)
+    j = max(w.max_shift, 1)
+    shifted = torch.empty((j, total), dtype=torch.int64, device=dev)
+    mask = torch.empty((j + 1, total), dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    route = thd.Route(w.n_slots, cp, total)
+    h = route.handle
+    rb = w.row_bytes
+    n_slots = w.n_slots
+    s_handle = stream.cuda_stream
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(events=None):
+        if events is not None:
+            e = [ev() for _ in range(2 + 4 * layers + 2)]
+            events.append(e)
+            e[0].record(stream)
+        thd.thd_build_route(h, cu, n_slots, cp, total, s_handle)
+        if events is not None:
+            e[1].record(stream)
+        for layer in range(layers):
+            if events is not None:
+                e[2 + 4 * layer].record(stream)
+            thd.thd_swap(h, thd.Z2C, x, a, total, rb, s_handle)
+            if events is not None:
+                e[3 + 4 * layer].record(stream)
+                e[4 + 4 * layer].record(stream)
+            thd.thd_swap(h, thd.C2Z, a, b, total, rb, s_handle)
+            if events is not None:
+                e[5 + 4 * layer].record(stream)
+        if events is not None:
+            e[-2].record(stream)
+        thd.thd_roll_labels(ids, cu, cu_real, n_slots, total, j, 0, shifted, mask, status, s_handle)
+        if events is not None:
+            e[-1].record(stream)
+
+    # correctness guard (not timed): one step, then the round trip must be exact
+    step()
+    torch.cuda.synchronize()
+    assert route.status() == 0 and int(status.item()) == 0
+    assert torch.equal(b.view(torch.int16), x.view(torch.int16))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel events on the launch stream
+    events = []
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(events)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
+
+    swap_ms, build_ms, roll_ms = [], [], []
+    for e in events:
+        build_ms.append(e[0].elapsed_time(e[1]))
+        for layer in range(layers):
+            swap_ms.append(e[2 + 4 * layer].elapsed_time(e[3 + 4 * layer]))
+            swap_ms.append(e[4 + 4 * layer].elapsed_time(e[5 + 4 * layer]))
+        roll_ms.append(e[-2].elapsed_time(e[-1]))
+    swap_avg_ms = float(np.mean(swap_ms))
+    swap_bytes, roll_bytes, total_bytes = step_bytes(w, layers)
+    swap_gbps = swap_bytes / (swap_avg_ms * 1e-3) / 1e9
+
+    # route build: host enqueue time of the build call alone (device time from the events above)
+    torch.cuda.synchronize()
+    enq = []
+    for _ in range(50):
+        t0 = time.perf_counter()
+        thd.thd_build_route(h, cu, n_slots, cp, total, s_handle)
+        enq.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+
+    # no call waits for the GPU: hold the stream with a spin kernel, enqueue a step
+    torch.cuda.synchronize()
+    gate = ev()
+    torch.cuda._sleep(int(5e8))
+    gate.record(stream)
+    step()
+    host_syncs = 0 if not gate.query() else None
+    torch.cuda.synchronize()
+
+    # context: a plain device-to-device copy of the same bytes
+    copy_ms = []
+    for _ in range(10):
+        c0, c1 = ev(), ev()
+        c0.record(stream)
+        a.copy_(x)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(c0.elapsed_time(c1))
+    copy_gbps = swap_bytes / (float(np.median(copy_ms)) * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = oracle_baseline(w, layers, args.cpu_seconds)
+
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "thd_swap GB/s (% HBM peak) + tokens/s; route-build latency, host syncs=0",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "cp_size": cp,
+            "tokens": total,
+            "slots": n_slots,
+            "rows": f"[{total},{','.join(str(s) for s in w.row_shape)}] bf16 (moved as bytes)",
+            "row_bytes": rb,
+            "step": f"build + {layers}x(z2c + c2z) + roll(max_shift={j})",
+        },
+        "swap_us": round(swap_avg_ms * 1e3, 2),
+        "swap_gbps": round(swap_gbps, 1),
+        "swap_tokens_per_s": round(total / (swap_avg_ms * 1e-3)),
+        "step_tokens_per_s": round(total / (ms_per_step * 1e-3)),
+        "route_build_us": round(float(np.median(build_ms)) * 1e3, 2),
+        "route_build_enqueue_us": round(float(np.median(enq)) * 1e6, 2),
+        "roll_us": round(float(np.median(roll_ms)) * 1e3, 2),
+        "host_syncs": host_syncs,
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(swap_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(swap_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    route.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,124 @@
+"""THD context-parallel layout transform on MI355X (gfx950).
+
+Low level: the C entry points of libthdcp under their own names
+(``thd_build_route``, ``thd_swap``, ``thd_roll_labels``, ...), see
+``binding.py`` and ``include/thd_cp.h``.
+
+High level: ``Route`` (one per micro-batch: build once, swap many times) and
+``roll_labels``.  Both only allocate output tensors with torch and hand
+pointers to the library; the work runs in the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+from .binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    THD_CONTIGUOUS_TO_ZIGZAG,
+    THD_ERR_ALIAS,
+    THD_ERR_ARG,
+    THD_ERR_CAPACITY,
+    THD_ERR_CU_DIVISIBLE,
+    THD_ERR_CU_MONOTONE,
+    THD_ERR_CU_START,
+    THD_ERR_CU_TOTAL,
+    THD_ERR_DEVICE,
+    THD_ERR_DIRECTION,
+    THD_ERR_HIP,
+    THD_ERR_INTEGRITY,
+    THD_ERR_NOT_BUILT,
+    THD_ERR_REAL_GT_PADDED,
+    THD_ERR_SHAPE,
+    THD_IDENTITY,
+    THD_MAX_CP,
+    THD_MAX_SHIFT,
+    THD_OK,
+    THD_ZIGZAG_TO_CONTIGUOUS,
+    ThdError,
+    thd_build_route,
+    thd_roll_labels,
+    thd_route_copy_out,
+    thd_route_create,
+    thd_route_destroy,
+    thd_route_info,
+    thd_route_status,
+    thd_strerror,
+    thd_swap,
+    thd_swap_tuning,
+)
+
+Z2C = THD_ZIGZAG_TO_CONTIGUOUS
+C2Z = THD_CONTIGUOUS_TO_ZIGZAG
+
+
+class Route:
+    """A device-resident zigzag <-> contiguous route.
+
+    ``Route(max_slots, max_cp, max_tokens)`` allocates the workspace once;
+    ``build(cu_seqlens_padded, cp_size)`` rebuilds it for a new micro-batch
+    without waiting for the GPU; ``swap(x, direction)`` moves the rows of
+    ``x`` ([T, ...], token dimension first) and returns a new tensor, or ``x``
+    itself when the route is the identity.
+    """
+
+    def __init__(self, max_slots: int, max_cp: int, max_tokens: int):
+        self.handle = thd_route_create(max_slots, max_cp, max_tokens)
+        self.total = 0
+
+    def close(self):
+        if getattr(self, "handle", None):
+            thd_route_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def build(self, cu_seqlens_padded, cp_size: int, total_tokens: int | None = None, stream=None) -> "Route":
+        n_slots = int(cu_seqlens_padded.numel()) - 1
+        if total_tokens is None:
+            raise ValueError("total_tokens is required (the boundaries stay on the device)")
+        thd_build_route(self.handle, cu_seqlens_padded, n_slots, cp_size, total_tokens, stream)
+        self.total = int(total_tokens)
+        return self
+
+    def swap(self, x, direction: int, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(x, memory_format=torch.contiguous_format)
+        rows = x.shape[0] if x.dim() else 0
+        row_bytes = x.element_size() * (x.numel() // rows if rows else 1)
+        code = thd_swap(self.handle, direction, x, out, rows, max(row_bytes, 1), stream)
+        return x if code == THD_IDENTITY else out
+
+    def status(self, stream=None) -> int:
+        return thd_route_status(self.handle, stream)
+
+    def copy_out(self, stream=None):
+        return thd_route_copy_out(self.handle, stream)
+
+    def info(self) -> dict:
+        return thd_route_info(self.handle)
+
+
+def roll_labels(ids, cu_seqlens_padded, cu_seqlens=None, max_shift: int = 1, fill: int = 0, stream=None,
+                with_status: bool = True):
+    """Shifted label streams [max_shift, T] (int64), masks [max_shift + 1, T]
+    (uint8) and, if asked, a device status word (int32 [1])."""
+    import torch
+    total = int(ids.numel())
+    shifted = torch.empty((max_shift, total), dtype=torch.int64, device=ids.device)
+    mask = torch.empty((max_shift + 1, total), dtype=torch.uint8, device=ids.device)
+    status = torch.empty(1, dtype=torch.int32, device=ids.device) if with_status else None
+    n_slots = int(cu_seqlens_padded.numel()) - 1
+    thd_roll_labels(ids, cu_seqlens_padded, cu_seqlens, n_slots, total, max_shift, fill, shifted, mask, status,
+                    stream)
+    return shifted, mask, status

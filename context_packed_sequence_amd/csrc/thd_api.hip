@@ -1,0 +1,281 @@
+// C ABI of libthdcp: host-side argument checks, the route object and
+// stream-ordered launches.  See include/thd_cp.h for the contract of each call.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "thd_internal.h"
+
+using thdcp::RouteDev;
+using thdcp::RunPair;
+
+struct thd_route {
+  int device = -1;
+  int32_t max_slots = 0;
+  int32_t max_cp = 0;
+  int64_t max_tokens = 0;
+  int64_t run_cap = 0;
+  int64_t dir_cap = 0;
+  void* base = nullptr;
+  RouteDev dev{};
+  // shape of the last build (host-known, so no call ever needs a device read)
+  int built = 0;
+  int32_t cp = 0;
+  int64_t total = 0;
+  int32_t n_slots = 0;
+};
+
+namespace {
+
+thdcp::SwapLaunch g_swap_cfg{64 * 1024, 0, 1};
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool on_route_device(const thd_route* r) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  return dev == r->device;
+}
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (a_bytes <= 0 || b_bytes <= 0) return false;
+  const auto x = reinterpret_cast<uintptr_t>(a);
+  const auto y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uint64_t>(b_bytes) && y < x + static_cast<uint64_t>(a_bytes);
+}
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* thd_strerror(int32_t code) {
+  switch (code) {
+    case THD_OK: return "ok";
+    case THD_IDENTITY: return "identity route: nothing written, use the input";
+    case THD_ERR_ARG: return "invalid argument";
+    case THD_ERR_DIRECTION: return "invalid direction";
+    case THD_ERR_NOT_BUILT: return "route was never built";
+    case THD_ERR_ALIAS: return "input and output ranges overlap";
+    case THD_ERR_CAPACITY: return "size exceeds the route's capacity";
+    case THD_ERR_SHAPE: return "row count differs from the route's total tokens";
+    case THD_ERR_HIP: return "HIP runtime error";
+    case THD_ERR_DEVICE: return "current device is not the route's device";
+    case THD_ERR_CU_START: return "cu_seqlens[0] is not 0";
+    case THD_ERR_CU_MONOTONE: return "cu_seqlens decreases";
+    case THD_ERR_CU_TOTAL: return "cu_seqlens[-1] differs from total tokens";
+    case THD_ERR_CU_DIVISIBLE: return "a sequence length is not a multiple of 2*cp_size";
+    case THD_ERR_REAL_GT_PADDED: return "a real sequence length exceeds its padded length";
+    case THD_ERR_INTEGRITY: return "route integrity check failed";
+    default: return "unknown code";
+  }
+}
+
+int thd_route_create(int32_t max_slots, int32_t max_cp, int64_t max_tokens, thd_route** out) {
+  if (!out) return THD_ERR_ARG;
+  *out = nullptr;
+  if (max_slots < 1 || max_cp < 1 || max_cp > THD_MAX_CP || max_tokens < 1 || max_tokens > INT32_MAX)
+    return THD_ERR_ARG;
+  thd_route* r = new (std::nothrow) thd_route();
+  if (!r) return THD_ERR_ARG;
+  if (hipGetDevice(&r->device) != hipSuccess) {
+    delete r;
+    return THD_ERR_HIP;
+  }
+  r->max_slots = max_slots;
+  r->max_cp = max_cp;
+  r->max_tokens = max_tokens;
+  r->run_cap = 2LL * max_cp * max_slots + max_cp;
+  r->dir_cap = (max_tokens + thdcp::kDirBlock - 1) / thdcp::kDirBlock + 1;
+
+  int64_t off = 0;
+  const int64_t o_hdr = off;       off = align_up(off + thdcp::kHdrWords * 4, 256);
+  const int64_t o_src = off;       off = align_up(off + r->run_cap * 8, 256);
+  const int64_t o_dst = off;       off = align_up(off + r->run_cap * 8, 256);
+  const int64_t o_split = off;     off = align_up(off + static_cast<int64_t>(max_cp) * max_cp * 4, 256);
+  const int64_t o_dsrc = off;      off = align_up(off + r->dir_cap * 4, 256);
+  const int64_t o_ddst = off;      off = align_up(off + r->dir_cap * 4, 256);
+  const int64_t o_dstart = off;    off = align_up(off + static_cast<int64_t>(max_slots) * 4, 256);
+  const int64_t o_dlen = off;      off = align_up(off + static_cast<int64_t>(max_slots) * 4, 256);
+  if (hipMalloc(&r->base, static_cast<size_t>(off)) != hipSuccess) {
+    delete r;
+    return THD_ERR_HIP;
+  }
+  char* b = static_cast<char*>(r->base);
+  r->dev.hdr = reinterpret_cast<int32_t*>(b + o_hdr);
+  r->dev.runs_src = reinterpret_cast<RunPair*>(b + o_src);
+  r->dev.runs_dst = reinterpret_cast<RunPair*>(b + o_dst);
+  r->dev.split = reinterpret_cast<int32_t*>(b + o_split);
+  r->dev.dir_src = reinterpret_cast<int32_t*>(b + o_dsrc);
+  r->dev.dir_dst = reinterpret_cast<int32_t*>(b + o_ddst);
+  r->dev.doc_start = reinterpret_cast<int32_t*>(b + o_dstart);
+  r->dev.doc_len = reinterpret_cast<int32_t*>(b + o_dlen);
+  r->dev.run_cap = r->run_cap;
+  *out = r;
+  return THD_OK;
+}
+
+void thd_route_destroy(thd_route* route) {
+  if (!route) return;
+  if (route->base) {
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (prev != route->device) (void)hipSetDevice(route->device);
+    (void)hipFree(route->base);
+    if (prev >= 0 && prev != route->device) (void)hipSetDevice(prev);
+  }
+  delete route;
+}
+
+int thd_build_route(thd_route* route, const int32_t* cu_seqlens_padded, int32_t n_slots, int32_t cp_size,
+                    int64_t total_tokens, void* stream) {
+  if (!route || !cu_seqlens_padded || n_slots < 0 || cp_size < 1 || total_tokens < 0 || total_tokens > INT32_MAX)
+    return THD_ERR_ARG;
+  if (n_slots > route->max_slots || cp_size > route->max_cp || total_tokens > route->max_tokens)
+    return THD_ERR_CAPACITY;
+  if (!on_route_device(route)) return THD_ERR_DEVICE;
+  route->built = 0;
+  route->cp = cp_size;
+  route->total = total_tokens;
+  route->n_slots = n_slots;
+  if (cp_size == 1) {  // identity; the boundaries are not read
+    route->built = 1;
+    return THD_OK;
+  }
+  hipStream_t s = as_stream(stream);
+  if (thdcp::launch_route_build(cu_seqlens_padded, n_slots, cp_size, static_cast<int32_t>(total_tokens), route->dev,
+                                s) != hipSuccess)
+    return THD_ERR_HIP;
+  if (thdcp::launch_route_index(route->dev, static_cast<int32_t>(total_tokens), s) != hipSuccess) return THD_ERR_HIP;
+  route->built = 1;
+  return THD_OK;
+}
+
+int thd_swap(const thd_route* route, int32_t direction, const void* in, void* out, int64_t rows, int64_t row_bytes,
+             void* stream) {
+  if (!route || rows < 0 || row_bytes < 1) return THD_ERR_ARG;
+  if (direction != THD_ZIGZAG_TO_CONTIGUOUS && direction != THD_CONTIGUOUS_TO_ZIGZAG) return THD_ERR_DIRECTION;
+  if (!route->built) return THD_ERR_NOT_BUILT;
+  if (rows != route->total) return THD_ERR_SHAPE;
+  if (route->cp == 1 || rows == 0) return THD_IDENTITY;
+  if (!in || !out) return THD_ERR_ARG;
+  if (row_bytes > INT64_MAX / rows) return THD_ERR_ARG;
+  const int64_t bytes = rows * row_bytes;
+  if (overlaps(in, bytes, out, bytes)) return THD_ERR_ALIAS;
+  if (!on_route_device(route)) return THD_ERR_DEVICE;
+  const bool z2c = direction == THD_ZIGZAG_TO_CONTIGUOUS;
+  const RunPair* runs = z2c ? route->dev.runs_dst : route->dev.runs_src;
+  const int32_t* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
+  const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
+  if (thdcp::launch_swap(route->dev.hdr, runs, word, dir, in, out, static_cast<int32_t>(rows), row_bytes, g_swap_cfg,
+                         as_stream(stream)) != hipSuccess)
+    return THD_ERR_HIP;
+  return THD_OK;
+}
+
+int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const int32_t* cu_seqlens, int32_t n_slots,
+                    int64_t total_tokens, int32_t max_shift, int64_t fill, int64_t* shifted, uint8_t* mask,
+                    int32_t* status, void* stream) {
+  if (!cu_seqlens_padded || n_slots < 0 || total_tokens < 0 || total_tokens > INT32_MAX) return THD_ERR_ARG;
+  if (max_shift < 1 || max_shift > THD_MAX_SHIFT) return THD_ERR_ARG;
+  if (total_tokens > 0 && (!ids || !shifted || !mask)) return THD_ERR_ARG;
+  const int64_t t = total_tokens;
+  if (overlaps(shifted, t * max_shift * 8, ids, t * 8) || overlaps(mask, t * (max_shift + 1), ids, t * 8) ||
+      overlaps(mask, t * (max_shift + 1), shifted, t * max_shift * 8))
+    return THD_ERR_ALIAS;
+  if (status && (overlaps(status, 4, shifted, t * max_shift * 8) || overlaps(status, 4, mask, t * (max_shift + 1))))
+    return THD_ERR_ALIAS;
+  if (thdcp::launch_roll(ids, cu_seqlens_padded, cu_seqlens, n_slots, static_cast<int32_t>(total_tokens), max_shift,
+                         fill, shifted, mask, status, as_stream(stream)) != hipSuccess)
+    return THD_ERR_HIP;
+  return THD_OK;
+}
+
+int thd_route_status(const thd_route* route, void* stream, int32_t* host_status) {
+  if (!route || !host_status) return THD_ERR_ARG;
+  if (!route->built) return THD_ERR_NOT_BUILT;
+  if (route->cp == 1) {
+    *host_status = THD_OK;
+    return THD_OK;
+  }
+  if (!on_route_device(route)) return THD_ERR_DEVICE;
+  int32_t v = 0;
+  hipStream_t s = as_stream(stream);
+  if (hipMemcpyAsync(&v, route->dev.hdr + thdcp::kHdrStatus, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return THD_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return THD_ERR_HIP;
+  *host_status = v;
+  return THD_OK;
+}
+
+int thd_route_copy_out(const thd_route* route, void* stream, int32_t* host_n_runs, int32_t capacity,
+                       int32_t* host_runs_by_src, int32_t* host_runs_by_dst, int32_t* host_split) {
+  if (!route || !host_n_runs || capacity < 0) return THD_ERR_ARG;
+  if (!route->built) return THD_ERR_NOT_BUILT;
+  if (route->cp == 1) {
+    *host_n_runs = 0;
+    return THD_OK;
+  }
+  if (!on_route_device(route)) return THD_ERR_DEVICE;
+  hipStream_t s = as_stream(stream);
+  int32_t hdr[thdcp::kHdrWords];
+  if (hipMemcpyAsync(hdr, route->dev.hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess) return THD_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return THD_ERR_HIP;
+  const int32_t n = hdr[thdcp::kHdrStatus] == THD_OK ? hdr[thdcp::kHdrRunsSrc] : 0;
+  *host_n_runs = n;
+  if (n > capacity) return THD_ERR_CAPACITY;
+  const int32_t cp = route->cp;
+  const int64_t total = route->total;
+  std::vector<RunPair> a(static_cast<size_t>(n)), b(static_cast<size_t>(n));
+  if (n > 0) {
+    if (hipMemcpyAsync(a.data(), route->dev.runs_src, n * sizeof(RunPair), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(b.data(), route->dev.runs_dst, n * sizeof(RunPair), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return THD_ERR_HIP;
+  }
+  std::vector<int32_t> split(static_cast<size_t>(cp) * cp);
+  if (host_split &&
+      hipMemcpyAsync(split.data(), route->dev.split, split.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return THD_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return THD_ERR_HIP;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t next_a = i + 1 < n ? a[i + 1].out : total;
+    const int64_t next_b = i + 1 < n ? b[i + 1].out : total;
+    if (host_runs_by_src) {  // out = zigzag row, in = token
+      host_runs_by_src[3 * i + 0] = a[i].out;
+      host_runs_by_src[3 * i + 1] = a[i].in;
+      host_runs_by_src[3 * i + 2] = static_cast<int32_t>(next_a - a[i].out);
+    }
+    if (host_runs_by_dst) {  // out = token, in = zigzag row
+      host_runs_by_dst[3 * i + 0] = b[i].in;
+      host_runs_by_dst[3 * i + 1] = b[i].out;
+      host_runs_by_dst[3 * i + 2] = static_cast<int32_t>(next_b - b[i].out);
+    }
+  }
+  if (host_split) std::memcpy(host_split, split.data(), split.size() * 4);
+  return THD_OK;
+}
+
+int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_tokens, int32_t* n_slots,
+                   int32_t* built) {
+  if (!route) return THD_ERR_ARG;
+  if (cp_size) *cp_size = route->cp;
+  if (total_tokens) *total_tokens = route->total;
+  if (n_slots) *n_slots = route->n_slots;
+  if (built) *built = route->built;
+  return THD_OK;
+}
+
+int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal) {
+  if (tile_bytes < 0 || max_workgroups < 0 || nontemporal < -1 || nontemporal > 1) return THD_ERR_ARG;
+  if (tile_bytes > 0) g_swap_cfg.tile_bytes = tile_bytes;
+  g_swap_cfg.max_workgroups = max_workgroups;
+  if (nontemporal >= 0) g_swap_cfg.nontemporal = nontemporal;
+  return THD_OK;
+}
+
+}  // extern "C"

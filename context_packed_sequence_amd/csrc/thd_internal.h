@@ -1,0 +1,80 @@
+// Internal declarations shared by the translation units of libthdcp.
+// Not part of the public ABI (that is include/thd_cp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "thd_cp.h"
+
+namespace thdcp {
+
+// The run directory holds one entry per block of 1 << kDirShift rows.
+constexpr int kDirShift = 4;
+constexpr int kDirBlock = 1 << kDirShift;
+
+// Header words of the route workspace (int32).
+enum HeaderWord : int {
+  kHdrStatus = 0,     // THD_OK or a THD_ERR_* code written by the build kernel
+  kHdrRunsSrc = 1,    // runs in zigzag-row order
+  kHdrRunsDst = 2,    // runs in token (contiguous-row) order
+  kHdrDocs = 3,       // non-empty slots
+  kHdrCp = 4,
+  kHdrTotal = 5,
+  kHdrWords = 16,
+};
+
+// A run maps `len` consecutive input rows onto `len` consecutive output rows.
+// Stored as (first output row, first input row); the length is implied by the
+// next run's output row (or the total for the last run), because the runs of
+// one order tile the output rows without gaps.
+struct RunPair {
+  int32_t out;
+  int32_t in;
+};
+
+// Device pointers into the route workspace.
+struct RouteDev {
+  int32_t* hdr;
+  RunPair* runs_src;   // ordered by zigzag row: out = zigzag row, in = token
+  RunPair* runs_dst;   // ordered by token:      out = token,      in = zigzag row
+  int32_t* split;      // [cp][cp]
+  int32_t* dir_src;    // run index covering zigzag row 16*b
+  int32_t* dir_dst;    // run index covering token 16*b
+  int32_t* doc_start;  // compacted non-empty slots
+  int32_t* doc_len;
+  int64_t run_cap;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total,
+                              const RouteDev& ws, hipStream_t stream);
+hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream);
+
+struct SwapLaunch {
+  int64_t tile_bytes;
+  int32_t max_workgroups;
+  int32_t nontemporal;
+};
+hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const int32_t* dir,
+                       const void* in, void* out, int32_t total, int64_t row_bytes,
+                       const SwapLaunch& cfg, hipStream_t stream);
+
+hipError_t launch_roll(const int64_t* ids, const int32_t* cu_pad, const int32_t* cu_real,
+                       int32_t n_slots, int32_t total, int32_t max_shift, int64_t fill,
+                       int64_t* shifted, uint8_t* mask, int32_t* status, hipStream_t stream);
+
+// Severity of a validation failure: larger wins; 0 = no failure.
+__host__ __device__ inline int32_t severity_to_code(int sev) {
+  switch (sev) {
+    case 5: return THD_ERR_CU_START;
+    case 4: return THD_ERR_CU_MONOTONE;
+    case 3: return THD_ERR_CU_TOTAL;
+    case 2: return THD_ERR_CU_DIVISIBLE;
+    case 1: return THD_ERR_REAL_GT_PADDED;
+    default: return THD_OK;
+  }
+}
+constexpr int kSevStart = 5, kSevMonotone = 4, kSevTotal = 3, kSevDivisible = 2, kSevRealGtPadded = 1;
+
+}  // namespace thdcp

@@ -1,0 +1,114 @@
+// Document-aware label shift, MTP roll and valid-token mask in one pass.
+//
+// Page "Packed Sequence 与上下文并行": labels are the next token, but never
+// across a document (§1.3); each MTP depth needs the same care, one more
+// token ahead (§1.6); pads added per document for alignment (§2.2) carry no
+// label and are zero in the valid-token mask (§2.2, §3.4).  The pages do these
+// with a Python loop over documents and a separate MTP helper; here one kernel
+// writes every shifted stream and every mask.
+//
+// For position t in padded slot s, e = cu_pad[s] + real length of s is the end
+// of the document's real tokens:
+//   mask[0][t] = t < e
+//   shifted[j-1][t] = ids[t+j] and mask[j][t] = 1 when t + j < e, else fill / 0.
+//
+// Each workgroup first checks the whole boundary lists (cheap: a few hundred
+// ints from L2), so that a bad list stops every workgroup before it writes
+// anything; it stages the boundaries in LDS when they fit and its slice of
+// ids (plus max_shift tokens of look-ahead) in LDS, then gives each thread one
+// position: a binary search finds the slot, and the J shifted values and J+1
+// mask bytes are written with consecutive lanes on consecutive positions.
+#include "thd_internal.h"
+
+namespace thdcp {
+namespace {
+
+constexpr int kRollThreads = 256;
+constexpr int kRollLdsSlots = 4096;  // boundaries staged in LDS (dynamic, 8 B per slot, <= 32 KiB)
+
+template <bool kLds>
+__global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __restrict__ ids,
+                                                            const int32_t* __restrict__ cu_pad,
+                                                            const int32_t* __restrict__ cu_real, int32_t n_slots,
+                                                            int32_t total, int32_t max_shift, int64_t fill,
+                                                            int64_t* __restrict__ shifted,
+                                                            uint8_t* __restrict__ mask, int32_t* __restrict__ status) {
+  extern __shared__ int32_t s_cu[];                   // kLds: [n_slots + 1] padded, then [n_slots] real lengths
+  int32_t* s_pad = s_cu;
+  int32_t* s_len = s_cu + (n_slots + 1);
+  __shared__ int64_t s_ids[kRollThreads + THD_MAX_SHIFT];
+  __shared__ int s_sev;
+  const int tid = threadIdx.x;
+
+  if (tid == 0) s_sev = 0;
+  __syncthreads();
+  int sev = 0;
+  if (tid == 0) {
+    if (cu_pad[0] != 0 || (cu_real && cu_real[0] != 0)) sev = kSevStart;
+    if (cu_pad[n_slots] != total) sev = max(sev, kSevTotal);
+  }
+  for (int i = tid; i <= n_slots; i += kRollThreads) {
+    const int32_t p0 = cu_pad[i];
+    if constexpr (kLds) s_pad[i] = p0;
+    if (i < n_slots) {
+      const int32_t p1 = cu_pad[i + 1];
+      const int64_t plen = static_cast<int64_t>(p1) - p0;
+      int64_t rlen = plen;
+      if (cu_real) rlen = static_cast<int64_t>(cu_real[i + 1]) - cu_real[i];
+      if (plen < 0 || rlen < 0) sev = max(sev, kSevMonotone);
+      else if (rlen > plen) sev = max(sev, kSevRealGtPadded);
+      if constexpr (kLds) s_len[i] = static_cast<int32_t>(rlen);
+    }
+  }
+  if (sev) atomicMax(&s_sev, sev);
+  __syncthreads();
+  const int32_t code = severity_to_code(s_sev);
+  if (status && blockIdx.x == 0 && tid == 0) *status = code;
+  if (code != THD_OK) return;
+
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRollThreads;
+  if (t0 >= total) return;
+  const int n_load = static_cast<int>(min(static_cast<int64_t>(total) - t0, static_cast<int64_t>(kRollThreads + max_shift)));
+  for (int i = tid; i < n_load; i += kRollThreads) s_ids[i] = ids[t0 + i];
+  __syncthreads();
+
+  const int64_t t = t0 + tid;
+  if (t >= total) return;
+  // slot s: cu_pad[s] <= t < cu_pad[s + 1]; that slot is never empty
+  int32_t lo = 0, hi = n_slots;
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    const int32_t v = kLds ? s_pad[mid] : cu_pad[mid];
+    if (v <= t) lo = mid;
+    else hi = mid;
+  }
+  int64_t real_len;
+  if constexpr (kLds) real_len = s_len[lo];
+  else real_len = cu_real ? static_cast<int64_t>(cu_real[lo + 1]) - cu_real[lo]
+                          : static_cast<int64_t>(cu_pad[lo + 1]) - cu_pad[lo];
+  const int64_t e = static_cast<int64_t>(kLds ? s_pad[lo] : cu_pad[lo]) + real_len;
+  mask[t] = t < e ? 1 : 0;
+  for (int j = 1; j <= max_shift; ++j) {
+    const bool ok = t + j < e;
+    shifted[static_cast<int64_t>(j - 1) * total + t] = ok ? s_ids[tid + j] : fill;
+    mask[static_cast<int64_t>(j) * total + t] = ok ? 1 : 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_roll(const int64_t* ids, const int32_t* cu_pad, const int32_t* cu_real, int32_t n_slots,
+                       int32_t total, int32_t max_shift, int64_t fill, int64_t* shifted, uint8_t* mask,
+                       int32_t* status, hipStream_t stream) {
+  const int64_t blocks64 = total > 0 ? (static_cast<int64_t>(total) + kRollThreads - 1) / kRollThreads : 1;
+  const dim3 grid(static_cast<unsigned>(blocks64));
+  if (n_slots + 1 <= kRollLdsSlots)
+    hipLaunchKernelGGL(roll_kernel<true>, grid, dim3(kRollThreads), static_cast<size_t>(2 * n_slots + 1) * 4, stream,
+                       ids, cu_pad, cu_real, n_slots, total, max_shift, fill, shifted, mask, status);
+  else
+    hipLaunchKernelGGL(roll_kernel<false>, grid, dim3(kRollThreads), 0, stream, ids, cu_pad, cu_real, n_slots, total,
+                       max_shift, fill, shifted, mask, status);
+  return hipGetLastError();
+}
+
+}  // namespace thdcp

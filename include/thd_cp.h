@@ -1,0 +1,215 @@
+/*
+ * thd_cp.h -- C ABI of the THD context-parallel layout transform (MI355X, gfx950).
+ *
+ * Packed variable-length batches ("THD": tokens x heads x dim, documents laid
+ * end to end and described by a boundary list cu_seqlens) are sharded over cp
+ * context-parallel ranks in one of two token layouts:
+ *
+ *   zigzag     every padded document of length L is cut into 2*cp chunks of
+ *              L/(2*cp) tokens; rank r keeps chunk r and chunk 2*cp-1-r of
+ *              every document, documents in order, the earlier chunk first
+ *              (ring slice, page "Packed Sequence 与上下文并行", §2.4 and the
+ *              worked example of §3.5);
+ *   contiguous rank r keeps tokens [r*T/cp, (r+1)*T/cp) of the packed stream
+ *              (Ulysses slice, same page §2.5).
+ *
+ * Both layouts are unions of global token intervals, so the route between them
+ * is an interval intersection (Relax PR #273 "fla mcore chunkwise cp stage 3",
+ * §2.1).  This library builds that route on the GPU from the padded boundary
+ * list and applies it to row-major activations.  On one GPU the cross-rank
+ * exchange is emulated: a buffer holds every rank's share, rank 0 first
+ * ("emulated global rows": row = rank * T/cp + local row), and the swap is one
+ * global row permutation.
+ *
+ * Conventions for every call:
+ *  - pointers are device pointers unless the argument says "host";
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream); every
+ *    call is stream-ordered and returns without waiting for the GPU, except
+ *    the two marked SYNC;
+ *  - boundary lists are int32 [n_slots + 1], non-decreasing, starting at 0;
+ *    an empty slot (a repeated boundary) is allowed anywhere;
+ *  - the call must be made with the route's device current;
+ *  - return value: THD_OK (0), THD_IDENTITY (1, nothing written), or a
+ *    negative THD_ERR_* code.  Argument errors are detected on the host and
+ *    returned at once; errors that depend on boundary values are detected on
+ *    the GPU and written to a device status word (see thd_route_status).
+ *  - no call allocates or frees memory except thd_route_create/destroy, and
+ *    no call synchronises except thd_route_status and thd_route_copy_out.
+ */
+#ifndef THD_CP_H
+#define THD_CP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return and status codes ------------------------------------------ */
+#define THD_OK                  0
+#define THD_IDENTITY            1   /* swap is the identity: nothing written, use `in` */
+#define THD_ERR_ARG            -1   /* null pointer, negative size, cp < 1, ...        */
+#define THD_ERR_DIRECTION      -2   /* direction is neither of the two values below    */
+#define THD_ERR_NOT_BUILT      -3   /* route never built                               */
+#define THD_ERR_ALIAS          -4   /* input and output byte ranges overlap            */
+#define THD_ERR_CAPACITY       -5   /* n_slots / cp_size / total_tokens above create() */
+#define THD_ERR_SHAPE          -6   /* rows differs from the route's total_tokens      */
+#define THD_ERR_HIP            -7   /* a HIP runtime call or kernel launch failed      */
+#define THD_ERR_DEVICE         -8   /* current device differs from the route's device  */
+/* Written on the device, in this precedence (first rule that fails wins): */
+#define THD_ERR_CU_START      -10   /* cu[0] != 0                                      */
+#define THD_ERR_CU_MONOTONE   -11   /* cu[i+1] < cu[i] for some i                      */
+#define THD_ERR_CU_TOTAL      -12   /* cu[n_slots] != total_tokens                     */
+#define THD_ERR_CU_DIVISIBLE  -13   /* a slot length is not a multiple of 2*cp_size    */
+#define THD_ERR_REAL_GT_PADDED -14  /* roll: real length above padded length           */
+#define THD_ERR_INTEGRITY     -15   /* route self-check failed (internal error)        */
+
+/* ---- directions ---------------------------------------------------------- */
+#define THD_ZIGZAG_TO_CONTIGUOUS 0
+#define THD_CONTIGUOUS_TO_ZIGZAG 1
+
+/* ---- limits -------------------------------------------------------------- */
+#define THD_MAX_CP        1024
+#define THD_MAX_SHIFT     8
+
+typedef struct thd_route thd_route;   /* opaque; owns one device workspace */
+
+/*
+ * thd_route_create -- allocate a route able to hold any batch with at most
+ * `max_slots` slots, `max_cp` ranks and `max_tokens` tokens (all >= 1,
+ * max_cp <= THD_MAX_CP, max_tokens <= INT32_MAX).  The workspace lives on the
+ * current device: (2*max_cp*max_slots + max_cp) runs in each of two orders
+ * (8 B each), a max_cp^2 split matrix, two row directories of
+ * ceil(max_tokens/16) int32 entries, 2*max_slots int32 of scratch and a
+ * 64-byte header.  *out (host) receives the handle.  The only call that
+ * allocates device memory.  Returns THD_OK, THD_ERR_ARG or THD_ERR_HIP.
+ */
+int thd_route_create(int32_t max_slots, int32_t max_cp, int64_t max_tokens, thd_route** out);
+
+/* thd_route_destroy -- free the workspace (waits for the device to finish
+ * using it).  NULL is ignored. */
+void thd_route_destroy(thd_route* route);
+
+/*
+ * thd_build_route -- build the zigzag <-> contiguous route for one batch.
+ *
+ * cu_seqlens_padded: device int32 [n_slots + 1], the padded boundaries.  The
+ * route depends only on these boundaries and cp_size (Relax PR #273, §1 and
+ * §2.1), so one build serves every layer, both directions and the recompute
+ * replay of a micro-batch; rebuild it for the next micro-batch.
+ *
+ * One kernel with one workgroup validates the boundaries (codes
+ * THD_ERR_CU_START .. THD_ERR_CU_DIVISIBLE, in that precedence), drops empty
+ * slots, lays out the 2*cp zigzag segments of every document, cuts them at the
+ * contiguous ranks' borders and writes the maximal runs (in zigzag-row order
+ * and in token order) plus the cp x cp split matrix; a second, grid-wide
+ * kernel writes a directory of the run covering every 16th row.  Results and
+ * the status word stay on the device.
+ *
+ * cp_size == 1: the route is the identity; nothing is launched and the
+ * boundaries are not read (the swap short-circuits for one rank before any
+ * validation, Relax PR #273 §2.6).  cp_size above the route's max_cp, n_slots
+ * above max_slots or total_tokens above max_tokens: THD_ERR_CAPACITY.
+ * Rebuilding while swaps that use the route are still queued on another
+ * stream is a race the caller must avoid.
+ */
+int thd_build_route(thd_route* route, const int32_t* cu_seqlens_padded, int32_t n_slots,
+                    int32_t cp_size, int64_t total_tokens, void* stream);
+
+/*
+ * thd_swap -- apply the route to `rows` rows of `row_bytes` bytes each.
+ *
+ * THD_ZIGZAG_TO_CONTIGUOUS: `in` is the emulated zigzag buffer, `out` receives
+ * the emulated contiguous buffer (token order); THD_CONTIGUOUS_TO_ZIGZAG is
+ * the inverse.  Both buffers are row-major [rows, row_bytes] with the token
+ * dimension outermost (Relax PR #273 §2.6 moves it there first).  Rows are
+ * copied bit for bit; no arithmetic is done on them.  `in` and `out` must not
+ * overlap (THD_ERR_ALIAS): an in-place permutation is not supported.
+ * `rows` must equal the route's total_tokens (THD_ERR_SHAPE); any
+ * row_bytes >= 1 works, 16-byte multiples with 16-byte aligned pointers take
+ * the widest path.
+ *
+ * Returns THD_IDENTITY without launching when the route is the identity
+ * (cp_size == 1 or total_tokens == 0): the caller keeps `in` (zero copy, as
+ * the pages' identity route does).  If the route's device status is an error,
+ * the kernel writes nothing.  One kernel launch otherwise.
+ */
+int thd_swap(const thd_route* route, int32_t direction, const void* in, void* out,
+             int64_t rows, int64_t row_bytes, void* stream);
+
+/*
+ * thd_roll_labels -- document-aware label shift, MTP roll and valid-token mask
+ * in one pass ("Packed Sequence 与上下文并行" §1.3, §1.6, §2.2).
+ *
+ * ids:               device int64 [total_tokens], the packed token stream
+ *                    in natural (contiguous) order.
+ * cu_seqlens_padded: device int32 [n_slots + 1], padded boundaries (positions).
+ * cu_seqlens:        device int32 [n_slots + 1], real (unpadded) boundaries;
+ *                    NULL means no slot has pads.  The pads of a slot are the
+ *                    tail of its padded range.
+ * max_shift:         J in 1..THD_MAX_SHIFT.  Shift 1 is the next-token label,
+ *                    shift k+1 the target of MTP depth k.
+ * shifted:           device int64 [J][total_tokens] (output).
+ * mask:              device uint8 [J + 1][total_tokens] (output).
+ * status:            device int32 word or NULL; receives THD_OK or the first
+ *                    failing rule: THD_ERR_CU_START, THD_ERR_CU_MONOTONE (either
+ *                    list), THD_ERR_CU_TOTAL (padded list), then
+ *                    THD_ERR_REAL_GT_PADDED.  On such an error nothing else is
+ *                    written.
+ *
+ * For position t of slot s, with e = cu_seqlens_padded[s] + real length of s:
+ * mask[0][t] = (t < e); for j = 1..J, when t + j < e, shifted[j-1][t] =
+ * ids[t + j] and mask[j][t] = 1, else shifted[j-1][t] = fill and mask[j][t] =
+ * 0.  No target ever comes from another document or from a pad.  Outputs must
+ * not overlap each other or ids (THD_ERR_ALIAS).  One kernel launch.
+ */
+int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const int32_t* cu_seqlens,
+                    int32_t n_slots, int64_t total_tokens, int32_t max_shift, int64_t fill,
+                    int64_t* shifted, uint8_t* mask, int32_t* status, void* stream);
+
+/*
+ * thd_route_status -- SYNC.  Waits for `stream`, then stores the status word
+ * written by the last build into *host_status (host): THD_OK or one of
+ * THD_ERR_CU_* / THD_ERR_INTEGRITY.  For an identity route it stores THD_OK
+ * without touching the device.  Opt-in: the hot path never calls it.
+ */
+int thd_route_status(const thd_route* route, void* stream, int32_t* host_status);
+
+/*
+ * thd_route_copy_out -- SYNC.  Waits for `stream`, then copies the route to
+ * host memory for inspection: *host_n_runs = number of runs; if the pointers
+ * are non-NULL and `capacity` >= that number, host_runs_by_src and
+ * host_runs_by_dst (host int32 [capacity][3]) receive the runs as
+ * (zigzag row, contiguous row, length) triples in emulated global rows, sorted
+ * by zigzag row and by contiguous row respectively, and host_split (host
+ * int32 [cp][cp]) the split matrix: split[s][d] rows go from zigzag rank s to
+ * contiguous rank d.  An identity route reports 0 runs.  THD_ERR_CAPACITY if
+ * `capacity` is too small (only *host_n_runs is written then).
+ */
+int thd_route_copy_out(const thd_route* route, void* stream, int32_t* host_n_runs, int32_t capacity,
+                       int32_t* host_runs_by_src, int32_t* host_runs_by_dst, int32_t* host_split);
+
+/*
+ * thd_route_info -- host-only query of the last build's shape: cp_size,
+ * total_tokens, n_slots and whether it was built (each pointer may be NULL).
+ */
+int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_tokens,
+                   int32_t* n_slots, int32_t* built);
+
+/*
+ * thd_swap_tuning -- set the swap kernel's launch shape for later calls in
+ * this process: bytes per workgroup tile (0 keeps the default), a cap on the
+ * number of workgroups (0 = one workgroup per tile) and whether loads and
+ * stores are marked non-temporal (-1 keeps the default).  For launch-shape
+ * sweeps; the results of thd_swap do not depend on it.
+ */
+int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal);
+
+/* thd_strerror -- static text for a return or status code. */
+const char* thd_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THD_CP_H */

@@ -1,0 +1,97 @@
+"""The C-ABI library loads on the host and exports what include/thd_cp.h declares.
+
+CPU only: nothing here launches a kernel.  The error paths called below are the
+ones the library rejects on the host before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "thd_cp.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    names = re.findall(r"\b(?:int|void|const char\s*\*)\s+(thd_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def declared_constants():
+    text = open(HEADER, encoding="utf-8").read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(THD_[A-Z0-9_]+)\s+(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    import context_packed_sequence_amd as p
+    return p
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("thd_build_route", "thd_swap", "thd_roll_labels"):
+        assert n in names
+    assert len(names) >= 10
+
+
+def test_library_exports_every_declared_symbol(pkg):
+    lib = pkg.binding.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(pkg.EXPORTS) == set(declared_functions())
+
+
+def test_binding_constants_match_header(pkg):
+    for name, value in declared_constants().items():
+        assert getattr(pkg.binding, name) == value, name
+
+
+def test_strerror_covers_every_code(pkg):
+    for name, value in declared_constants().items():
+        if name.startswith("THD_ERR_") or name in ("THD_OK", "THD_IDENTITY"):
+            assert pkg.thd_strerror(value) != "unknown code", name
+    assert pkg.thd_strerror(12345) == "unknown code"
+
+
+def test_host_rejections_without_device_work(pkg):
+    lib = pkg.binding.library()
+    h = ctypes.c_void_p()
+    # bad create arguments are rejected before any HIP call
+    assert lib.thd_route_create(0, 2, 16, ctypes.byref(h)) == pkg.THD_ERR_ARG
+    assert lib.thd_route_create(4, 0, 16, ctypes.byref(h)) == pkg.THD_ERR_ARG
+    assert lib.thd_route_create(4, pkg.THD_MAX_CP + 1, 16, ctypes.byref(h)) == pkg.THD_ERR_ARG
+    assert lib.thd_route_create(4, 2, 2 ** 31, ctypes.byref(h)) == pkg.THD_ERR_ARG
+    assert lib.thd_route_create(4, 2, 16, None) == pkg.THD_ERR_ARG
+    # null route
+    assert lib.thd_build_route(None, 1, 1, 2, 8, None) == pkg.THD_ERR_ARG
+    assert lib.thd_swap(None, 0, 1, 2, 8, 4, None) == pkg.THD_ERR_ARG
+    n = ctypes.c_int32()
+    assert lib.thd_route_status(None, None, ctypes.byref(n)) == pkg.THD_ERR_ARG
+    assert lib.thd_route_copy_out(None, None, ctypes.byref(n), 0, None, None, None) == pkg.THD_ERR_ARG
+    assert lib.thd_route_info(None, None, None, None, None) == pkg.THD_ERR_ARG
+    # roll: shift out of range, null boundaries, overlapping outputs
+    assert lib.thd_roll_labels(8, 16, None, 1, 8, 0, 0, 4096, 8192, None, None) == pkg.THD_ERR_ARG
+    assert lib.thd_roll_labels(8, 16, None, 1, 8, 9, 0, 4096, 8192, None, None) == pkg.THD_ERR_ARG
+    assert lib.thd_roll_labels(8, None, None, 1, 8, 1, 0, 4096, 8192, None, None) == pkg.THD_ERR_ARG
+    assert lib.thd_roll_labels(4096, 16, None, 1, 8, 1, 0, 4096 + 8, 1 << 20, None, None) == pkg.THD_ERR_ALIAS
+    assert lib.thd_roll_labels(1 << 20, 16, None, 1, 8, 2, 0, 4096, 4096 + 64, None, None) == pkg.THD_ERR_ALIAS
+    # tuning argument checks
+    assert lib.thd_swap_tuning(-1, 0, -1) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, -1, -1) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, 0, 2) == pkg.THD_ERR_ARG
+
+
+def test_package_and_oracle_share_no_code():
+    # The oracle imports nothing from the package and vice versa.
+    pkg_dir = os.path.join(ROOT, "context_packed_sequence_amd")
+    for d, other in ((os.path.join(ROOT, "oracle"), "context_packed_sequence_amd"), (pkg_dir, "oracle")):
+        for f in os.listdir(d):
+            if f.endswith(".py"):
+                src = open(os.path.join(d, f), encoding="utf-8").read()
+                assert not re.search(rf"^\s*(from|import)\s+{other}\b", src, flags=re.M), (d, f)

@@ -1,0 +1,128 @@
+"""The five named workloads at full size, in the launch configuration the bench
+times (default swap tiles, one workgroup per tile, non-temporal streaming).
+
+* the route (runs in both orders, split matrix) equals the oracle's exactly;
+* every output row's origin is checked through a stamp: each input row's
+  first 8 bytes hold its row index, so the stamps read back from the output
+  must equal the oracle's source row for every output row;
+* sampled rows (random ones plus the first and last row of every run) are
+  compared byte for byte with the input row the oracle names;
+* z->c followed by c->z returns the input exactly; where the buffers fit
+  comfortably in host memory the whole output is also compared with the
+  oracle's swap.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import check_route_matches_oracle, dev_i32, dev_i64, oracle_source_rows, say
+
+pytestmark = pytest.mark.gpu
+
+FULL_COMPARE = {"tiny", "gdn128k", "sft", "full"}
+
+
+@pytest.fixture(scope="module")
+def thd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import context_packed_sequence_amd as thd
+    return thd
+
+
+def device_rows(w):
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(W.BASE_SEED + w.index)
+    x = torch.randn((w.total,) + tuple(w.row_shape), dtype=torch.bfloat16, device="cuda", generator=g)
+    x.view(w.total, -1).view(torch.int64)[:, 0] = torch.arange(w.total, device="cuda")
+    return x
+
+
+def sample_rows(runs, total, rng, n=4096):
+    idx = rng.integers(0, total, size=min(n, total))
+    edges = np.concatenate([runs[:, 1], runs[:, 1] + runs[:, 2] - 1, runs[:, 0], runs[:, 0] + runs[:, 2] - 1])
+    return np.unique(np.concatenate([idx, edges, [0, total - 1]]))
+
+
+@pytest.mark.parametrize("name", list(W.NAMES) + ["sft512"])
+def test_workload_parity(thd, name):
+    import torch
+    w = W.make(name)
+    total, cp = w.total, w.cp
+    say("workload", name, "T", total, "cp", cp, "slots", w.n_slots, "row_bytes", w.row_bytes)
+    route = thd.Route(w.n_slots, cp, total)
+    route.build(dev_i32(w.cu_padded), cp, total)
+    r = check_route_matches_oracle(route, w.cu_padded, cp, total)
+    runs = O.canonical_runs(r)
+    x = device_rows(w)
+    rng = np.random.default_rng(5)
+    for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+        say(" swap", name, direction)
+        out = route.swap(x, d)
+        torch.cuda.synchronize()
+        src = oracle_source_rows(r, direction)
+        stamps = out.view(total, -1).view(torch.int64)[:, 0].cpu().numpy()
+        assert np.array_equal(stamps, src)
+        rows = sample_rows(runs, total, rng)
+        rows_t = torch.from_numpy(rows).cuda()
+        got = out.view(total, -1).index_select(0, rows_t).view(torch.int16).cpu().numpy()
+        want = x.view(total, -1).index_select(0, torch.from_numpy(src[rows]).cuda()).view(torch.int16).cpu().numpy()
+        assert np.array_equal(got, want)
+        back = route.swap(out, thd.C2Z if d == thd.Z2C else thd.Z2C)
+        torch.cuda.synchronize()
+        assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+        if name in FULL_COMPARE:
+            xh = x.view(total, -1).view(torch.int16).cpu().numpy()
+            want_all = O.swap_rows(xh, w.cu_padded, cp, total, direction)
+            assert np.array_equal(out.view(total, -1).view(torch.int16).cpu().numpy(), want_all)
+        del out, back
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_microbatch_96_swaps_and_roll(thd):
+    # One route reused by 48 layers x (z->c, c->z), then the label/MTP roll.
+    import torch
+    w = W.make("full")
+    total, cp = w.total, w.cp
+    say("full micro-batch", total, cp)
+    route = thd.Route(w.n_slots, cp, total)
+    route.build(dev_i32(w.cu_padded), cp, total)
+    x = device_rows(w)
+    a = torch.empty_like(x)
+    b = torch.empty_like(x)
+    cur = x
+    for layer in range(w.layers):
+        route.swap(cur, thd.Z2C, out=a)
+        route.swap(a, thd.C2Z, out=b)
+        cur = b
+    torch.cuda.synchronize()
+    assert torch.equal(b.view(torch.int16), x.view(torch.int16))
+    r = O.build_route(w.cu_padded.tolist(), cp, total)
+    stamps = a.view(total, -1).view(torch.int64)[:, 0].cpu().numpy()
+    assert np.array_equal(stamps, oracle_source_rows(r, "z2c"))
+    ids = w.ids()
+    shifted, mask, status = thd.roll_labels(dev_i64(ids), dev_i32(w.cu_padded), dev_i32(w.cu_real), w.max_shift, 0)
+    torch.cuda.synchronize()
+    want_s, want_m = O.roll_labels(ids, w.cu_padded, w.cu_real, total, w.max_shift, 0)
+    assert int(status.item()) == 0
+    assert np.array_equal(shifted.cpu().numpy(), want_s)
+    assert np.array_equal(mask.cpu().numpy(), want_m)
+    # valid-token count identity: sum of the mask equals the sum of real lengths
+    assert int(mask[0].sum().item()) == int(np.diff(w.cu_real).sum())
+
+
+@pytest.mark.parametrize("name", ["tiny", "gdn128k", "sft"])
+def test_workload_roll(thd, name):
+    import torch
+    w = W.make(name)
+    ids = w.ids()
+    say("roll workload", name)
+    shifted, mask, status = thd.roll_labels(dev_i64(ids), dev_i32(w.cu_padded), dev_i32(w.cu_real), 4, -1)
+    torch.cuda.synchronize()
+    want_s, want_m = O.roll_labels(ids, w.cu_padded, w.cu_real, w.total, 4, -1)
+    assert int(status.item()) == 0
+    assert np.array_equal(shifted.cpu().numpy(), want_s)
+    assert np.array_equal(mask.cpu().numpy(), want_m)

@@ -1,0 +1,202 @@
+"""GPU parity: libthdcp against the CPU oracle, byte for byte.
+
+Everything here is integer index work and bit copies, so the bar is exact
+equality: the route (runs in both orders and the split matrix), every swapped
+byte, every label and every mask byte.  Cases are small enough for the oracle
+to finish in seconds but span many swap tiles and end in a ragged tail.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import check_route_matches_oracle, dev_i32, dev_i64, expected_route, oracle_source_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def thd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import context_packed_sequence_amd as thd
+    return thd
+
+
+def build(thd, cu, cp, total, max_slots=None, max_cp=None):
+    route = thd.Route(max_slots or max(1, len(cu) - 1), max_cp or cp, max(total, 1))
+    route.build(dev_i32(cu), cp, total)
+    return route
+
+
+# ---- the test matrix of the Relax PR #273 page, §5: cp x direction x shape ----
+
+SHAPES = {
+    "single": [0, 48],
+    "unequal": [0, 16, 64, 96, 208],
+    "repeated": [0, 0, 32, 32, 32, 96, 160, 160],
+}
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("direction", ["z2c", "c2z"])
+@pytest.mark.parametrize("cp", [1, 2, 4, 8])
+def test_matrix_route_and_swap(thd, cp, direction, shape):
+    import torch
+    base = SHAPES[shape]
+    unit = 2 * cp
+    cu = [v // 16 * unit for v in base]          # same shape, lengths scaled to multiples of 2*cp
+    total = cu[-1]
+    say("matrix", cp, direction, shape, cu)
+    route = build(thd, cu, cp, total)
+    x = torch.randint(0, 256, (total, 24), dtype=torch.uint8, device="cuda")
+    d = thd.Z2C if direction == "z2c" else thd.C2Z
+    out = route.swap(x, d)
+    torch.cuda.synchronize()
+    if cp == 1:
+        assert out is x
+        return
+    check_route_matches_oracle(route, cu, cp, total)
+    want = O.swap_rows(x.cpu().numpy(), cu, cp, total, direction)
+    assert np.array_equal(out.cpu().numpy(), want)
+    # neighbouring ranks agree on split sizes: sender row s == receiver column s
+    _, _, split = route.copy_out()
+    r, _ = expected_route(cu, cp, total)
+    for s in range(cp):
+        assert split[s, :].tolist() == r["input_split_sizes"][s].tolist()
+        assert split[:, s].tolist() == r["output_split_sizes"][s].tolist()
+
+
+# ---- random ragged batches, many row sizes and alignments ----
+
+RANDOM_CASES = [
+    # seed, cp, docs, max_chunk, empty slots, row bytes, byte offset of both buffers
+    (0, 2, 9, 40, 0, 32, 0),
+    (1, 4, 40, 64, 3, 16, 0),
+    (2, 8, 25, 20, 8, 4096, 0),
+    (3, 3, 30, 50, 2, 12, 0),
+    (4, 4, 33, 48, 1, 4, 4),
+    (5, 2, 50, 70, 5, 6, 2),
+    (6, 5, 21, 30, 0, 3, 1),
+    (7, 16, 12, 9, 4, 8192, 0),
+    (8, 4, 60, 40, 6, 4112, 0),
+    (9, 8, 7, 200, 2, 8, 8),
+    (10, 6, 1, 500, 3, 1, 0),
+    (11, 2, 200, 8, 40, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"seed{c[0]}" for c in RANDOM_CASES])
+def test_random_swap_parity(thd, case):
+    import torch
+    seed, cp, docs, max_chunk, n_empty, rb, offset = case
+    w = W.random_packed(seed, cp, docs, max_chunk, n_empty, row_shape=(rb,), row_dtype="uint8")
+    cu, total = w.cu_padded, w.total
+    say("random", case, "T", total, "slots", w.n_slots)
+    route = build(thd, cu, cp, total)
+    check_route_matches_oracle(route, cu, cp, total)
+    x_host = w.rows_host()
+    nbytes = total * rb
+    in_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+    out_buf = torch.full((nbytes + 64,), 0xCD, dtype=torch.uint8, device="cuda")
+    in_buf[offset:offset + nbytes] = torch.from_numpy(x_host.reshape(-1)).cuda()
+    for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+        out_buf.fill_(0xCD)
+        code = thd.thd_swap(route.handle, d, in_buf.data_ptr() + offset, out_buf.data_ptr() + offset, total, rb)
+        assert code == thd.THD_OK
+        torch.cuda.synchronize()
+        got = out_buf.cpu().numpy()
+        want = O.swap_rows(x_host, cu, cp, total, direction).reshape(-1)
+        assert np.array_equal(got[offset:offset + nbytes], want), direction
+        # guard bands on both sides stay untouched
+        assert (got[:offset] == 0xCD).all() and (got[offset + nbytes:] == 0xCD).all()
+
+
+@pytest.mark.parametrize("tile_bytes,max_wg,nt", [(1, 0, 1), (1, 7, 0), (1 << 20, 3, 1), (4096, 1, 0)])
+def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt):
+    import torch
+    w = W.random_packed(42, 4, 30, 60, 3, row_shape=(48,), row_dtype="uint8")
+    cu, total = w.cu_padded, w.total
+    say("launch shape", tile_bytes, max_wg, nt, "T", total)
+    route = build(thd, cu, 4, total)
+    x = torch.from_numpy(w.rows_host()).cuda()
+    try:
+        thd.thd_swap_tuning(tile_bytes, max_wg, nt)
+        out = route.swap(x, thd.Z2C)
+        back = route.swap(out, thd.C2Z)
+        torch.cuda.synchronize()
+    finally:
+        thd.thd_swap_tuning(64 * 1024, 0, 1)
+    want = O.swap_rows(w.rows_host(), cu, 4, total, "z2c")
+    assert np.array_equal(out.cpu().numpy(), want)
+    assert torch.equal(back, x)
+
+
+# ---- label shift / MTP roll / valid mask ----
+
+ROLL_CASES = [
+    # seed, docs, max_chunk, empty, pad_max, max_shift, fill
+    (0, 5, 4, 0, 0, 1, 0),
+    (1, 40, 30, 5, 7, 4, 0),
+    (2, 300, 3, 20, 3, 8, -1),
+    (3, 64, 100, 1, 50, 2, 7),
+    (4, 1, 2000, 2, 1, 3, 0),
+]
+
+
+@pytest.mark.parametrize("case", ROLL_CASES, ids=[f"seed{c[0]}" for c in ROLL_CASES])
+def test_roll_parity(thd, case):
+    import torch
+    seed, docs, max_chunk, n_empty, pad_max, j, fill = case
+    w = W.random_packed(seed, 2, docs, max_chunk, n_empty, pad_max=pad_max)
+    total = w.total
+    ids = w.ids()
+    say("roll", case, "T", total)
+    shifted, mask, status = thd.roll_labels(dev_i64(ids), dev_i32(w.cu_padded), dev_i32(w.cu_real), j, fill)
+    torch.cuda.synchronize()
+    want_s, want_m = O.roll_labels(ids, w.cu_padded, w.cu_real, total, j, fill)
+    assert int(status.item()) == 0
+    assert np.array_equal(shifted.cpu().numpy(), want_s)
+    assert np.array_equal(mask.cpu().numpy(), want_m)
+    # without real boundaries: every slot is all real tokens
+    shifted, mask, status = thd.roll_labels(dev_i64(ids), dev_i32(w.cu_padded), None, j, fill)
+    torch.cuda.synchronize()
+    want_s, want_m = O.roll_labels(ids, w.cu_padded, None, total, j, fill)
+    assert np.array_equal(shifted.cpu().numpy(), want_s)
+    assert np.array_equal(mask.cpu().numpy(), want_m)
+
+
+def test_roll_many_slots_global_path(thd):
+    # more boundaries than the kernel stages in LDS: the global-memory search path
+    import torch
+    w = W.random_packed(77, 1, 9000, 3, 500, pad_max=2)
+    total = w.total
+    assert w.n_slots + 1 > 4096
+    ids = w.ids()
+    say("roll global path", w.n_slots, total)
+    shifted, mask, status = thd.roll_labels(dev_i64(ids), dev_i32(w.cu_padded), dev_i32(w.cu_real), 3, -5)
+    torch.cuda.synchronize()
+    want_s, want_m = O.roll_labels(ids, w.cu_padded, w.cu_real, total, 3, -5)
+    assert int(status.item()) == 0
+    assert np.array_equal(shifted.cpu().numpy(), want_s)
+    assert np.array_equal(mask.cpu().numpy(), want_m)
+
+
+def test_worked_example_on_gpu(thd, golden):
+    # The page's packed stream of §3.4 through the device path: per-rank tokens
+    # of §3.6 and the valid mask / count of §3.4 and §3.8.
+    import torch
+    g = golden("p3_worked_example.txt")
+    cu_pad = [int(v) for v in g["cu_seqlens_padded"]]
+    cu = [int(v) for v in g["cu_seqlens"]]
+    stream = np.frombuffer("".join(g["tokens"]).encode(), dtype=np.uint8).copy()
+    route = build(thd, cu_pad, 2, 16)
+    z = route.swap(torch.from_numpy(stream).cuda().view(16, 1), thd.C2Z)
+    got = z.cpu().numpy().reshape(-1).tobytes().decode()
+    assert got[:8] == "".join(g["rank0_tokens"]) and got[8:] == "".join(g["rank1_tokens"])
+    _, mask, status = thd.roll_labels(dev_i64(stream.astype(np.int64)), dev_i32(cu_pad), dev_i32(cu), 1, 0)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert mask[0].cpu().numpy().tolist() == [int(v) for v in g["valid_mask"]]
+    assert int(mask[0].sum().item()) == int(g["valid_total"][0])
