@@ -72,7 +72,7 @@ def _load() -> ctypes.CDLL:
         "thd_route_copy_out": (ctypes.c_int, [c_p, c_p, ctypes.POINTER(c_i32), c_i32, c_p, c_p, c_p]),
         "thd_route_info": (ctypes.c_int, [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i64),
                                           ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]),
-        "thd_swap_tuning": (ctypes.c_int, [c_i64, c_i32, c_i32]),
+        "thd_swap_tuning": (ctypes.c_int, [c_i64, c_i32, c_i32, c_i32, c_i32]),
         "thd_strerror": (ctypes.c_char_p, [c_i32]),
     }
     for name, (res, args) in sig.items():
@@ -179,8 +179,11 @@ def thd_route_info(route: int) -> dict:
     return {"cp_size": cp.value, "total_tokens": total.value, "n_slots": n_slots.value, "built": bool(built.value)}
 
 
-def thd_swap_tuning(tile_bytes: int = 0, max_workgroups: int = 0, nontemporal: int = -1) -> None:
-    _check(_lib.thd_swap_tuning(tile_bytes, max_workgroups, nontemporal), "thd_swap_tuning")
+def thd_swap_tuning(tile_bytes: int = 0, max_workgroups: int = 0, nontemporal: int = 1,
+                    block_threads: int = 0, tile_order: int = 0) -> None:
+    """Override the swap launch shape (0 = built-in choice); no arguments restore the defaults."""
+    _check(_lib.thd_swap_tuning(tile_bytes, max_workgroups, nontemporal, block_threads, tile_order),
+           "thd_swap_tuning")
 
 
 def library():

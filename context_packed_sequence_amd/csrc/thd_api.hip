@@ -31,7 +31,7 @@ struct thd_route {
 
 namespace {
 
-thdcp::SwapLaunch g_swap_cfg{64 * 1024, 0, 1};
+thdcp::SwapLaunch g_swap_cfg{0, 0, 1, 0, 0};
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -98,8 +98,8 @@ int thd_route_create(int32_t max_slots, int32_t max_cp, int64_t max_tokens, thd_
   const int64_t o_src = off;       off = align_up(off + r->run_cap * 8, 256);
   const int64_t o_dst = off;       off = align_up(off + r->run_cap * 8, 256);
   const int64_t o_split = off;     off = align_up(off + static_cast<int64_t>(max_cp) * max_cp * 4, 256);
-  const int64_t o_dsrc = off;      off = align_up(off + r->dir_cap * 4, 256);
-  const int64_t o_ddst = off;      off = align_up(off + r->dir_cap * 4, 256);
+  const int64_t o_dsrc = off;      off = align_up(off + r->dir_cap * 16, 256);
+  const int64_t o_ddst = off;      off = align_up(off + r->dir_cap * 16, 256);
   const int64_t o_dstart = off;    off = align_up(off + static_cast<int64_t>(max_slots) * 4, 256);
   const int64_t o_dlen = off;      off = align_up(off + static_cast<int64_t>(max_slots) * 4, 256);
   if (hipMalloc(&r->base, static_cast<size_t>(off)) != hipSuccess) {
@@ -111,8 +111,8 @@ int thd_route_create(int32_t max_slots, int32_t max_cp, int64_t max_tokens, thd_
   r->dev.runs_src = reinterpret_cast<RunPair*>(b + o_src);
   r->dev.runs_dst = reinterpret_cast<RunPair*>(b + o_dst);
   r->dev.split = reinterpret_cast<int32_t*>(b + o_split);
-  r->dev.dir_src = reinterpret_cast<int32_t*>(b + o_dsrc);
-  r->dev.dir_dst = reinterpret_cast<int32_t*>(b + o_ddst);
+  r->dev.dir_src = reinterpret_cast<thdcp::DirEntry*>(b + o_dsrc);
+  r->dev.dir_dst = reinterpret_cast<thdcp::DirEntry*>(b + o_ddst);
   r->dev.doc_start = reinterpret_cast<int32_t*>(b + o_dstart);
   r->dev.doc_len = reinterpret_cast<int32_t*>(b + o_dlen);
   r->dev.run_cap = r->run_cap;
@@ -170,7 +170,7 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
   if (!on_route_device(route)) return THD_ERR_DEVICE;
   const bool z2c = direction == THD_ZIGZAG_TO_CONTIGUOUS;
   const RunPair* runs = z2c ? route->dev.runs_dst : route->dev.runs_src;
-  const int32_t* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
+  const thdcp::DirEntry* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
   const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
   if (thdcp::launch_swap(route->dev.hdr, runs, word, dir, in, out, static_cast<int32_t>(rows), row_bytes, g_swap_cfg,
                          as_stream(stream)) != hipSuccess)
@@ -270,11 +270,15 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
   return THD_OK;
 }
 
-int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal) {
-  if (tile_bytes < 0 || max_workgroups < 0 || nontemporal < -1 || nontemporal > 1) return THD_ERR_ARG;
-  if (tile_bytes > 0) g_swap_cfg.tile_bytes = tile_bytes;
-  g_swap_cfg.max_workgroups = max_workgroups;
-  if (nontemporal >= 0) g_swap_cfg.nontemporal = nontemporal;
+int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
+                    int32_t tile_order) {
+  if (tile_bytes < 0 || max_workgroups < 0 || nontemporal < 0 || nontemporal > 1 || tile_order < 0 ||
+      tile_order > 2)
+    return THD_ERR_ARG;
+  if (block_threads != 0 && block_threads != 128 && block_threads != 256 && block_threads != 512 &&
+      block_threads != 1024)
+    return THD_ERR_ARG;
+  g_swap_cfg = thdcp::SwapLaunch{tile_bytes, max_workgroups, nontemporal, block_threads, tile_order};
   return THD_OK;
 }
 

@@ -33,14 +33,23 @@ struct RunPair {
   int32_t in;
 };
 
+// Directory entry for output row 16*b: everything a swap tile starting there
+// needs to begin copying, in one 16-byte load.
+struct DirEntry {
+  int32_t in;       // input row that feeds output row 16*b
+  int32_t run_end;  // first output row after the run that holds 16*b
+  int32_t run;      // index of that run
+  int32_t pad;
+};
+
 // Device pointers into the route workspace.
 struct RouteDev {
   int32_t* hdr;
   RunPair* runs_src;   // ordered by zigzag row: out = zigzag row, in = token
   RunPair* runs_dst;   // ordered by token:      out = token,      in = zigzag row
   int32_t* split;      // [cp][cp]
-  int32_t* dir_src;    // run index covering zigzag row 16*b
-  int32_t* dir_dst;    // run index covering token 16*b
+  DirEntry* dir_src;   // entry for zigzag row 16*b (c->z output rows)
+  DirEntry* dir_dst;   // entry for token 16*b (z->c output rows)
   int32_t* doc_start;  // compacted non-empty slots
   int32_t* doc_len;
   int64_t run_cap;
@@ -51,12 +60,15 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
                               const RouteDev& ws, hipStream_t stream);
 hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream);
 
+// Swap launch overrides; 0 in a field means the built-in choice.
 struct SwapLaunch {
   int64_t tile_bytes;
   int32_t max_workgroups;
-  int32_t nontemporal;
+  int32_t nontemporal;    // 1 on, 0 off
+  int32_t block_threads;  // 128, 256, 512 or 1024
+  int32_t tile_order;     // 1 natural, 2 XCD-grouped
 };
-hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const int32_t* dir,
+hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                        const void* in, void* out, int32_t total, int64_t row_bytes,
                        const SwapLaunch& cfg, hipStream_t stream);
 

@@ -264,13 +264,24 @@ __device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, in
   return lo;
 }
 
-__global__ __launch_bounds__(256) void route_index_kernel(RouteDev ws, int32_t n_blocks) {
+__device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t n, int32_t row, int32_t total) {
+  const int32_t k = last_run_at_or_before(runs, n, row);
+  const RunPair r = runs[k];
+  DirEntry e;
+  e.in = r.in + (row - r.out);
+  e.run_end = k + 1 < n ? runs[k + 1].out : total;
+  e.run = k;
+  e.pad = 0;
+  return e;
+}
+
+__global__ __launch_bounds__(256) void route_index_kernel(RouteDev ws, int32_t n_blocks, int32_t total) {
   if (ws.hdr[kHdrStatus] != THD_OK) return;
   const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= n_blocks) return;
   const int32_t row = b << kDirShift;
-  ws.dir_src[b] = last_run_at_or_before(ws.runs_src, ws.hdr[kHdrRunsSrc], row);
-  ws.dir_dst[b] = last_run_at_or_before(ws.runs_dst, ws.hdr[kHdrRunsDst], row);
+  ws.dir_src[b] = dir_entry(ws.runs_src, ws.hdr[kHdrRunsSrc], row, total);
+  ws.dir_dst[b] = dir_entry(ws.runs_dst, ws.hdr[kHdrRunsDst], row, total);
 }
 
 }  // namespace
@@ -284,7 +295,7 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
 hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream) {
   const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
   if (n_blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_index_kernel, dim3((n_blocks + 255) / 256), dim3(256), 0, stream, ws, n_blocks);
+  hipLaunchKernelGGL(route_index_kernel, dim3((n_blocks + 255) / 256), dim3(256), 0, stream, ws, n_blocks, total);
   return hipGetLastError();
 }
 

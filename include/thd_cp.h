@@ -80,7 +80,7 @@ typedef struct thd_route thd_route;   /* opaque; owns one device workspace */
  * max_cp <= THD_MAX_CP, max_tokens <= INT32_MAX).  The workspace lives on the
  * current device: (2*max_cp*max_slots + max_cp) runs in each of two orders
  * (8 B each), a max_cp^2 split matrix, two row directories of
- * ceil(max_tokens/16) int32 entries, 2*max_slots int32 of scratch and a
+ * ceil(max_tokens/16) + 1 entries of 16 B, 2*max_slots int32 of scratch and a
  * 64-byte header.  *out (host) receives the handle.  The only call that
  * allocates device memory.  Returns THD_OK, THD_ERR_ARG or THD_ERR_HIP.
  */
@@ -103,7 +103,8 @@ void thd_route_destroy(thd_route* route);
  * slots, lays out the 2*cp zigzag segments of every document, cuts them at the
  * contiguous ranks' borders and writes the maximal runs (in zigzag-row order
  * and in token order) plus the cp x cp split matrix; a second, grid-wide
- * kernel writes a directory of the run covering every 16th row.  Results and
+ * kernel writes, for every 16th output row of each direction, the input row
+ * feeding it, the end of its run and the run's index.  Results and
  * the status word stay on the device.
  *
  * cp_size == 1: the route is the identity; nothing is launched and the
@@ -197,13 +198,22 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
                    int32_t* n_slots, int32_t* built);
 
 /*
- * thd_swap_tuning -- set the swap kernel's launch shape for later calls in
- * this process: bytes per workgroup tile (0 keeps the default), a cap on the
- * number of workgroups (0 = one workgroup per tile) and whether loads and
- * stores are marked non-temporal (-1 keeps the default).  For launch-shape
- * sweeps; the results of thd_swap do not depend on it.
+ * thd_swap_tuning -- override the swap kernel's launch shape for later calls
+ * in this process (a process-wide setting; not safe to change while another
+ * thread calls thd_swap).  For launch-shape sweeps: the results of thd_swap
+ * never depend on it.  A 0 selects the built-in choice for that field.
+ *   tile_bytes      output bytes per workgroup tile, rounded up to whole rows
+ *                   (built-in: 4 KiB for rows under 8 KiB, one row otherwise)
+ *   max_workgroups  cap on workgroups; above it workgroups loop over tiles
+ *   nontemporal     1: non-temporal loads and stores (built-in), 0: plain
+ *   block_threads   128, 256, 512 or 1024 for the 16-byte path
+ *   tile_order      1: tile b to workgroup b; 2: XCD-grouped (each of the 8
+ *                   XCDs streams one contiguous eighth of the output);
+ *                   built-in: grouped for rows of 8 KiB and more
+ * thd_swap_tuning(0, 0, 1, 0, 0) restores the built-in shape.
  */
-int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal);
+int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
+                    int32_t tile_order);
 
 /* thd_strerror -- static text for a return or status code. */
 const char* thd_strerror(int32_t code);

@@ -82,9 +82,12 @@ def test_host_rejections_without_device_work(pkg):
     assert lib.thd_roll_labels(4096, 16, None, 1, 8, 1, 0, 4096 + 8, 1 << 20, None, None) == pkg.THD_ERR_ALIAS
     assert lib.thd_roll_labels(1 << 20, 16, None, 1, 8, 2, 0, 4096, 4096 + 64, None, None) == pkg.THD_ERR_ALIAS
     # tuning argument checks
-    assert lib.thd_swap_tuning(-1, 0, -1) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, -1, -1) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, 0, 2) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(-1, 0, 1, 0, 0) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, -1, 1, 0, 0) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, 0, 2, 0, 0) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, 0, 1, 300, 0) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, 0, 1, 0, 3) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, 0, 1, 0, 0) == pkg.THD_OK
 
 
 def test_package_and_oracle_share_no_code():

@@ -113,21 +113,26 @@ def test_random_swap_parity(thd, case):
         assert (got[:offset] == 0xCD).all() and (got[offset + nbytes:] == 0xCD).all()
 
 
-@pytest.mark.parametrize("tile_bytes,max_wg,nt", [(1, 0, 1), (1, 7, 0), (1 << 20, 3, 1), (4096, 1, 0)])
-def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt):
+@pytest.mark.parametrize("tile_bytes,max_wg,nt,block,order,rb", [
+    (1, 0, 1, 256, 1, 48), (1, 7, 0, 512, 2, 48), (1 << 20, 3, 1, 1024, 1, 48), (4096, 1, 0, 128, 2, 48),
+    (20000, 0, 1, 512, 1, 4096), (20000, 5, 0, 1024, 2, 4096), (1000, 0, 1, 128, 2, 4096),
+    (3 * 4096, 13, 1, 256, 1, 4096), (0, 0, 1, 0, 0, 8192), (0, 9, 1, 0, 0, 8192), (0, 0, 0, 0, 0, 8208),
+    (0, 0, 1, 0, 0, 4096), (0, 6, 1, 0, 0, 4096), (0, 0, 1, 0, 2, 2048), (5000, 0, 1, 0, 2, 36),
+])
+def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt, block, order, rb):
     import torch
-    w = W.random_packed(42, 4, 30, 60, 3, row_shape=(48,), row_dtype="uint8")
+    w = W.random_packed(42, 4, 30, 60, 3, row_shape=(rb,), row_dtype="uint8")
     cu, total = w.cu_padded, w.total
-    say("launch shape", tile_bytes, max_wg, nt, "T", total)
+    say("launch shape", tile_bytes, max_wg, nt, block, order, rb, "T", total)
     route = build(thd, cu, 4, total)
     x = torch.from_numpy(w.rows_host()).cuda()
     try:
-        thd.thd_swap_tuning(tile_bytes, max_wg, nt)
+        thd.thd_swap_tuning(tile_bytes, max_wg, nt, block, order)
         out = route.swap(x, thd.Z2C)
         back = route.swap(out, thd.C2Z)
         torch.cuda.synchronize()
     finally:
-        thd.thd_swap_tuning(64 * 1024, 0, 1)
+        thd.thd_swap_tuning()
     want = O.swap_rows(w.rows_host(), cu, 4, total, "z2c")
     assert np.array_equal(out.cpu().numpy(), want)
     assert torch.equal(back, x)
