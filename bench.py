@@ -52,6 +52,29 @@ def step_bytes(w, layers):
     return swap, roll, 2 * layers * swap + roll
 
 
+def measured_traffic(workload):
+    """HBM bytes per swap launch from the committed counter summary of this
+    workload, or None when there is none or the swap kernel's source has
+    changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"swap_traffic_{workload}.txt")
+    src = os.path.join(ROOT, "context_packed_sequence_amd", "csrc", "thd_swap.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -269,7 +292,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(swap_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
         "cpu_baseline": cpu,
     }

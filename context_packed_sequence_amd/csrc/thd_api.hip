@@ -100,8 +100,7 @@ int thd_route_create(int32_t max_slots, int32_t max_cp, int64_t max_tokens, thd_
   const int64_t o_split = off;     off = align_up(off + static_cast<int64_t>(max_cp) * max_cp * 4, 256);
   const int64_t o_dsrc = off;      off = align_up(off + r->dir_cap * 16, 256);
   const int64_t o_ddst = off;      off = align_up(off + r->dir_cap * 16, 256);
-  const int64_t o_dstart = off;    off = align_up(off + static_cast<int64_t>(max_slots) * 4, 256);
-  const int64_t o_dlen = off;      off = align_up(off + static_cast<int64_t>(max_slots) * 4, 256);
+  const int64_t o_docs = off;      off = align_up(off + 3 * static_cast<int64_t>(max_slots) * 4, 256);
   if (hipMalloc(&r->base, static_cast<size_t>(off)) != hipSuccess) {
     delete r;
     return THD_ERR_HIP;
@@ -113,8 +112,8 @@ int thd_route_create(int32_t max_slots, int32_t max_cp, int64_t max_tokens, thd_
   r->dev.split = reinterpret_cast<int32_t*>(b + o_split);
   r->dev.dir_src = reinterpret_cast<thdcp::DirEntry*>(b + o_dsrc);
   r->dev.dir_dst = reinterpret_cast<thdcp::DirEntry*>(b + o_ddst);
-  r->dev.doc_start = reinterpret_cast<int32_t*>(b + o_dstart);
-  r->dev.doc_len = reinterpret_cast<int32_t*>(b + o_dlen);
+  r->dev.docs = reinterpret_cast<int32_t*>(b + o_docs);
+  r->dev.docs_cap = max_slots;
   r->dev.run_cap = r->run_cap;
   *out = r;
   return THD_OK;

@@ -50,8 +50,8 @@ struct RouteDev {
   int32_t* split;      // [cp][cp]
   DirEntry* dir_src;   // entry for zigzag row 16*b (c->z output rows)
   DirEntry* dir_dst;   // entry for token 16*b (z->c output rows)
-  int32_t* doc_start;  // compacted non-empty slots
-  int32_t* doc_len;
+  int32_t* docs;       // compacted non-empty slots: [start | chunk | offset], docs_cap each
+  int32_t docs_cap;
   int64_t run_cap;
 };
 

@@ -31,13 +31,6 @@ namespace {
 constexpr int kBuildThreads = 1024;
 constexpr int kBuildWaves = kBuildThreads / 64;
 
-// Make global-memory writes of the whole workgroup visible to all its threads.
-__device__ __forceinline__ void wg_sync_global() {
-  __threadfence();
-  __syncthreads();
-  __threadfence();
-}
-
 // Exclusive prefix sum over the workgroup.  Every thread must call it; it
 // returns the thread's exclusive offset and the workgroup total in *total.
 __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
@@ -76,61 +69,96 @@ struct Segment {
   int32_t rank;  // zigzag (source) rank
 };
 
-__device__ __forceinline__ Segment make_segment(const int32_t* doc_start, const int32_t* doc_len, int k,
-                                                int q, int cp, int share) {
-  const int32_t a = doc_start[k];
-  const int32_t c = doc_len[k] / (2 * cp);
+// Compacted document k: start token a_k, chunk length c_k = L_k / (2 cp) and
+// its local row in every rank's zigzag share, a_k / cp.  Stored as three
+// arrays of `cap` entries: [start | chunk | offset].
+struct Doc {
+  int32_t a, c, off;
+};
+
+__device__ __forceinline__ Doc load_doc(const int32_t* docs, int32_t cap, int32_t k) {
+  return Doc{docs[k], docs[cap + k], docs[2 * cap + k]};
+}
+
+// Chunk q of a document as a zigzag segment.
+__device__ __forceinline__ Segment chunk_segment(const Doc& d, int32_t q, int32_t cp, int32_t share) {
   const bool back = q >= cp;
   Segment s;
   s.rank = back ? 2 * cp - 1 - q : q;
-  s.tok = a + q * c;
-  s.src = s.rank * share + a / cp + (back ? c : 0);
-  s.len = c;
+  s.tok = d.a + q * d.c;
+  s.src = s.rank * share + d.off + (back ? d.c : 0);
+  s.len = d.c;
   return s;
 }
 
-// Segment j in zigzag-row order: rank-major, then document, then front/back.
-__device__ __forceinline__ Segment segment_src_order(const int32_t* ds, const int32_t* dl, int64_t j, int n_docs,
-                                                     int cp, int share) {
-  const int r = static_cast<int>(j / (2 * n_docs));
-  const int rem = static_cast<int>(j % (2 * n_docs));
-  const int k = rem >> 1;
-  const int q = (rem & 1) ? 2 * cp - 1 - r : r;
-  return make_segment(ds, dl, k, q, cp, share);
+// Cuts of a segment at the contiguous ranks' borders (multiples of `share`):
+// first destination rank and 1 or 2 pieces (a chunk is at most half a share).
+struct Cut {
+  int32_t first_d, rem, pieces;
+};
+
+__device__ __forceinline__ Cut cut_segment(const Segment& s, int32_t share) {
+  Cut c;
+  c.first_d = s.tok / share;
+  c.rem = s.tok - c.first_d * share;
+  c.pieces = (c.rem + s.len > share) ? 2 : 1;
+  return c;
 }
 
-// Segment j in token order: document-major, then chunk.
-__device__ __forceinline__ Segment segment_tok_order(const int32_t* ds, const int32_t* dl, int64_t j, int cp,
-                                                     int share) {
-  const int k = static_cast<int>(j / (2 * cp));
-  const int q = static_cast<int>(j % (2 * cp));
-  return make_segment(ds, dl, k, q, cp, share);
-}
+// The build kernel keeps the compacted documents and the split matrix in LDS
+// when 4 * (3 * n_slots + cp * cp) bytes fit in kBuildLdsBytes; otherwise it
+// uses the route's global scratch and global atomics (same steps, slower).
+constexpr int kBuildLdsBytes = 60 * 1024;
 
+template <bool kLds>
 __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
                                                                     int32_t cp, int32_t total, RouteDev ws) {
+  extern __shared__ int32_t s_dyn[];  // kLds: docs[3 * n_slots], split[cp * cp]
   __shared__ int s_wave[kBuildWaves + 1];
   __shared__ int s_sev;
   const int tid = threadIdx.x;
+  const int32_t cap = kLds ? n_slots : ws.docs_cap;
+  int32_t* docs = kLds ? s_dyn : ws.docs;
+  int32_t* split = kLds ? s_dyn + 3 * n_slots : ws.split;
 
-  // ---- 1. validate (precedence: start, monotone, total, divisibility) ----
   if (tid == 0) s_sev = 0;
-  for (int i = tid; i < cp * cp; i += kBuildThreads)
-    __hip_atomic_store(&ws.split[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wg_sync_global();
+  for (int i = tid; i < cp * cp; i += kBuildThreads) {
+    if constexpr (kLds) split[i] = 0;
+    else __hip_atomic_store(&split[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- 1+2. validate (precedence: start, monotone, total, divisibility) and
+  //           compact the non-empty slots, in one pass over the boundaries ----
   int sev = 0;
   if (tid == 0) {
     if (cu[0] != 0) sev = kSevStart;
     if (cu[n_slots] != total) sev = max(sev, kSevTotal);
   }
-  const int64_t two_cp = 2 * static_cast<int64_t>(cp);
-  for (int i = tid; i < n_slots; i += kBuildThreads) {
-    const int64_t a = cu[i], b = cu[i + 1];
-    if (b < a) sev = max(sev, kSevMonotone);
-    else if ((b - a) % two_cp != 0) sev = max(sev, kSevDivisible);
+  const int32_t two_cp = 2 * cp;
+  int32_t n_docs = 0;
+  for (int32_t base = 0; base < n_slots; base += kBuildThreads) {
+    const int32_t i = base + tid;
+    int32_t a = 0, len = 0;
+    if (i < n_slots) {
+      a = cu[i];
+      const int64_t d = static_cast<int64_t>(cu[i + 1]) - a;
+      if (d < 0) sev = max(sev, kSevMonotone);
+      else if (d % two_cp != 0) sev = max(sev, kSevDivisible);
+      else len = static_cast<int32_t>(d);
+    }
+    int sum;
+    const int off = block_exclusive_scan(len > 0 ? 1 : 0, s_wave, &sum);
+    if (len > 0) {
+      const int32_t k = n_docs + off;
+      docs[k] = a;
+      docs[cap + k] = len / two_cp;
+      docs[2 * cap + k] = a / cp;
+    }
+    n_docs += sum;
   }
   if (sev) atomicMax(&s_sev, sev);
-  __syncthreads();
+  if constexpr (!kLds) __threadfence();  // global path: zeroed split and document list are complete
+  __syncthreads();                       // publishes the document list to the whole workgroup
   if (s_sev) {
     if (tid == 0) {
       ws.hdr[kHdrRunsSrc] = 0;
@@ -143,103 +171,95 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     return;
   }
 
-  // ---- 2. compact: drop empty slots (repeated boundaries) ----
-  int n_docs = 0;
-  for (int base = 0; base < n_slots; base += kBuildThreads) {
-    const int i = base + tid;
-    int32_t a = 0, len = 0;
-    if (i < n_slots) {
-      a = cu[i];
-      len = cu[i + 1] - a;
-    }
-    int sum;
-    const int off = block_exclusive_scan(len > 0 ? 1 : 0, s_wave, &sum);
-    if (len > 0) {
-      ws.doc_start[n_docs + off] = a;
-      ws.doc_len[n_docs + off] = len;
-    }
-    n_docs += sum;
-  }
-  wg_sync_global();
-
-  const int share = total / cp;  // T/cp rows per rank (T is a multiple of 2*cp here)
-  const int64_t n_seg = two_cp * n_docs;
+  // Valid boundaries: T is a multiple of 2*cp and every segment holds at least
+  // one token, so the 2*cp*n_docs segment indices fit in int32.
+  const int32_t share = total / cp;
+  const int32_t n_seg = two_cp * n_docs;
+  const int32_t two_n = 2 * n_docs;
   bool overflow = false;
 
-  // ---- 3. runs in zigzag-row order, plus the split matrix ----
-  int n_src = 0;
-  for (int64_t base = 0; base < n_seg; base += kBuildThreads) {
-    const int64_t j = base + tid;
-    int count = 0, merge = 0, first_d = 0, pieces = 0;
-    Segment s{};
+  // ---- 3+4. runs in zigzag-row order (with the split matrix) and in token
+  //           order.  Thread j looks at segment j of each order, counts the
+  //           runs that start in it, and one scan of both counts (packed
+  //           into 16-bit halves: at most 2048 per pass) places them. ----
+  int32_t n_src = 0, n_dst = 0;
+  for (int32_t base = 0; base < n_seg; base += kBuildThreads) {
+    const int32_t j = base + tid;
+    int32_t merge_s = 0, merge_t = 0;
+    Segment ss{}, st{};
+    Cut cs{0, 0, 0}, ct{0, 0, 0};
     if (j < n_seg) {
-      s = segment_src_order(ws.doc_start, ws.doc_len, j, n_docs, cp, share);
-      first_d = s.tok / share;
-      pieces = (s.tok + s.len - 1) / share - first_d + 1;
-      if (s.src % share != 0 && s.tok % share != 0) {
-        const Segment p = segment_src_order(ws.doc_start, ws.doc_len, j - 1, n_docs, cp, share);
-        merge = (p.tok + p.len == s.tok) ? 1 : 0;
+      // zigzag-row order: rank-major, then document, then front/back chunk
+      const int32_t r = j / two_n;
+      const int32_t rem = j - r * two_n;
+      const int32_t k = rem >> 1;
+      const bool back = rem & 1;
+      const Doc dk = load_doc(docs, cap, k);
+      ss = chunk_segment(dk, back ? two_cp - 1 - r : r, cp, share);
+      cs = cut_segment(ss, share);
+      if (rem > 0 && cs.rem != 0) {  // not the first row of a source share, not on a destination border
+        const Doc dp = back ? dk : load_doc(docs, cap, k - 1);
+        const Segment p = chunk_segment(dp, back ? r : two_cp - 1 - r, cp, share);
+        merge_s = (p.tok + p.len == ss.tok) ? 1 : 0;
       }
-      count = pieces - merge;
+      // token order: document-major, then chunk
+      const int32_t kt = j / two_cp;
+      const int32_t q = j - kt * two_cp;
+      const Doc dt = load_doc(docs, cap, kt);
+      st = chunk_segment(dt, q, cp, share);
+      ct = cut_segment(st, share);
+      if (j > 0 && !(kt == 0 && q < cp) && ct.rem != 0) {
+        const Doc dp = q > 0 ? dt : load_doc(docs, cap, kt - 1);
+        const Segment p = chunk_segment(dp, q > 0 ? q - 1 : two_cp - 1, cp, share);
+        merge_t = (p.src + p.len == st.src) ? 1 : 0;
+      }
     }
+    const int count_s = j < n_seg ? cs.pieces - merge_s : 0;
+    const int count_t = j < n_seg ? ct.pieces - merge_t : 0;
     int sum;
-    const int off = block_exclusive_scan(count, s_wave, &sum);
+    const int off = block_exclusive_scan(count_s | (count_t << 16), s_wave, &sum);
     if (j < n_seg) {
-      for (int p = 0; p < pieces; ++p) {
-        const int32_t ptok = p == 0 ? s.tok : (first_d + p) * share;
-        const int32_t pend = min(s.tok + s.len, (first_d + p + 1) * share);
-        atomicAdd(&ws.split[s.rank * cp + first_d + p], pend - ptok);
-        if (p >= merge) {
-          const int64_t slot = static_cast<int64_t>(n_src) + off + p - merge;
-          if (slot < ws.run_cap) ws.runs_src[slot] = RunPair{s.src + (ptok - s.tok), ptok};
+      const int32_t off_s = off & 0xFFFF, off_t = off >> 16;
+      for (int p = 0; p < cs.pieces; ++p) {
+        const int32_t ptok = p == 0 ? ss.tok : (cs.first_d + p) * share;
+        const int32_t pend = min(ss.tok + ss.len, (cs.first_d + p + 1) * share);
+        atomicAdd(&split[ss.rank * cp + cs.first_d + p], pend - ptok);
+        if (p >= merge_s) {
+          const int64_t slot = static_cast<int64_t>(n_src) + off_s + p - merge_s;
+          if (slot < ws.run_cap) ws.runs_src[slot] = RunPair{ss.src + (ptok - ss.tok), ptok};
           else overflow = true;
         }
       }
-    }
-    n_src += sum;
-  }
-
-  // ---- 4. the same runs in token order ----
-  int n_dst = 0;
-  for (int64_t base = 0; base < n_seg; base += kBuildThreads) {
-    const int64_t j = base + tid;
-    int count = 0, merge = 0, first_d = 0, pieces = 0;
-    Segment s{};
-    if (j < n_seg) {
-      s = segment_tok_order(ws.doc_start, ws.doc_len, j, cp, share);
-      first_d = s.tok / share;
-      pieces = (s.tok + s.len - 1) / share - first_d + 1;
-      if (j > 0 && s.src % share != 0 && s.tok % share != 0) {
-        const Segment p = segment_tok_order(ws.doc_start, ws.doc_len, j - 1, cp, share);
-        merge = (p.src + p.len == s.src) ? 1 : 0;
-      }
-      count = pieces - merge;
-    }
-    int sum;
-    const int off = block_exclusive_scan(count, s_wave, &sum);
-    if (j < n_seg) {
-      for (int p = merge; p < pieces; ++p) {
-        const int32_t ptok = p == 0 ? s.tok : (first_d + p) * share;
-        const int64_t slot = static_cast<int64_t>(n_dst) + off + p - merge;
-        if (slot < ws.run_cap) ws.runs_dst[slot] = RunPair{ptok, s.src + (ptok - s.tok)};
+      for (int p = merge_t; p < ct.pieces; ++p) {
+        const int32_t ptok = p == 0 ? st.tok : (ct.first_d + p) * share;
+        const int64_t slot = static_cast<int64_t>(n_dst) + off_t + p - merge_t;
+        if (slot < ws.run_cap) ws.runs_dst[slot] = RunPair{ptok, st.src + (ptok - st.tok)};
         else overflow = true;
       }
     }
-    n_dst += sum;
+    n_src += sum & 0xFFFF;
+    n_dst += sum >> 16;
   }
-  wg_sync_global();
+  if constexpr (!kLds) __threadfence();  // global path: every split atomic has landed
+  __syncthreads();
 
   // ---- 5. integrity: same run count both ways; each rank sends and receives T/cp ----
-  if (tid == 0) s_sev = 0;
-  __syncthreads();
   bool bad = overflow || n_src != n_dst;
   for (int i = tid; i < cp; i += kBuildThreads) {
     int64_t row = 0, col = 0;
     for (int d = 0; d < cp; ++d) {
-      row += __hip_atomic_load(&ws.split[i * cp + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      col += __hip_atomic_load(&ws.split[d * cp + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (kLds) {
+        row += split[i * cp + d];
+        col += split[d * cp + i];
+      } else {
+        row += __hip_atomic_load(&split[i * cp + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        col += __hip_atomic_load(&split[d * cp + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (row != share || col != share) bad = true;
+  }
+  if constexpr (kLds) {
+    for (int i = tid; i < cp * cp; i += kBuildThreads) ws.split[i] = split[i];
   }
   if (bad) atomicMax(&s_sev, 1);
   __syncthreads();
@@ -253,9 +273,8 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   }
 }
 
-// Largest i in [0, n) with runs[i].out <= row (runs[0].out == 0 <= row).
-__device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, int32_t n, int32_t row) {
-  int32_t lo = 0, hi = n;  // runs[lo].out <= row, and runs[hi].out > row or hi == n
+// Largest i in [lo, hi) with runs[i].out <= row, given runs[lo].out <= row.
+__device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, int32_t lo, int32_t hi, int32_t row) {
   while (hi - lo > 1) {
     const int32_t mid = (lo + hi) >> 1;
     if (runs[mid].out <= row) lo = mid;
@@ -264,38 +283,105 @@ __device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, in
   return lo;
 }
 
-__device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t n, int32_t row, int32_t total) {
-  const int32_t k = last_run_at_or_before(runs, n, row);
-  const RunPair r = runs[k];
-  DirEntry e;
-  e.in = r.in + (row - r.out);
-  e.run_end = k + 1 < n ? runs[k + 1].out : total;
-  e.run = k;
-  e.pad = 0;
-  return e;
+// The same search done by one wave: each round, 64 lanes probe 64 evenly
+// spaced runs and a ballot keeps the interval that holds the answer, so a
+// list of up to 4096 runs takes two dependent loads instead of twelve.
+__device__ __forceinline__ int32_t wave_last_run_at_or_before(const RunPair* runs, int32_t n, int32_t row,
+                                                              int lane) {
+  int32_t lo = 0, hi = n;  // runs[lo].out <= row (runs[0].out == 0); answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int32_t step = (hi - lo + 63) / 64;
+    const int32_t idx = lo + lane * step;
+    const bool le = idx < hi && runs[idx].out <= row;
+    const uint64_t m = __ballot(le);  // a prefix of the lanes; lane 0 is always set
+    const int last = 63 - __clzll(static_cast<long long>(m));
+    lo += last * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
 }
 
-__global__ __launch_bounds__(256) void route_index_kernel(RouteDev ws, int32_t n_blocks, int32_t total) {
+constexpr int kIndexThreads = 256;   // four waves: one search each (2 directions x window ends)
+constexpr int kIndexStage = 1024;    // runs of one window staged in LDS up to this many
+
+// Directory: for every 16th output row of each direction, the input row that
+// feeds it, the end of its run and the run index.  A workgroup covers 256
+// directory rows; its four waves first find the runs at both ends of that row
+// window (per direction), the window's runs are staged in LDS, and each
+// thread then searches only that short list.
+__global__ __launch_bounds__(kIndexThreads) void route_index_kernel(RouteDev ws, int32_t n_blocks, int32_t total) {
+  __shared__ int32_t s_k[2][2];
+  __shared__ RunPair s_runs[2][kIndexStage];
   if (ws.hdr[kHdrStatus] != THD_OK) return;
-  const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t b0 = blockIdx.x * kIndexThreads;
+  const int32_t b_last = min(n_blocks, b0 + kIndexThreads) - 1;
+  const int32_t n_runs[2] = {ws.hdr[kHdrRunsDst], ws.hdr[kHdrRunsSrc]};
+  const RunPair* runs[2] = {ws.runs_dst, ws.runs_src};
+  DirEntry* dir[2] = {ws.dir_dst, ws.dir_src};
+  {
+    const int d = wave >> 1;
+    const int32_t row = (wave & 1) ? (b_last << kDirShift) : (b0 << kDirShift);
+    const int32_t k = wave_last_run_at_or_before(runs[d], n_runs[d], row, lane);
+    if (lane == 0) s_k[d][wave & 1] = k;
+  }
+  __syncthreads();
+  bool staged[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int32_t k_lo = s_k[d][0];
+    const int32_t cnt = min(s_k[d][1] + 2, n_runs[d]) - k_lo;  // window's runs plus the one after
+    staged[d] = cnt <= kIndexStage;
+    if (staged[d])
+      for (int i = tid; i < cnt; i += kIndexThreads) s_runs[d][i] = runs[d][k_lo + i];
+  }
+  __syncthreads();
+  const int32_t b = b0 + tid;
   if (b >= n_blocks) return;
   const int32_t row = b << kDirShift;
-  ws.dir_src[b] = dir_entry(ws.runs_src, ws.hdr[kHdrRunsSrc], row, total);
-  ws.dir_dst[b] = dir_entry(ws.runs_dst, ws.hdr[kHdrRunsDst], row, total);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int32_t k_lo = s_k[d][0], k_hi = s_k[d][1];
+    int32_t k;
+    RunPair r;
+    int32_t run_end;
+    if (staged[d]) {
+      k = k_lo + last_run_at_or_before(s_runs[d], 0, k_hi - k_lo + 1, row);
+      r = s_runs[d][k - k_lo];
+      run_end = k + 1 < n_runs[d] ? s_runs[d][k + 1 - k_lo].out : total;
+    } else {
+      k = last_run_at_or_before(runs[d], k_lo, k_hi + 1, row);
+      r = runs[d][k];
+      run_end = k + 1 < n_runs[d] ? runs[d][k + 1].out : total;
+    }
+    DirEntry e;
+    e.in = r.in + (row - r.out);
+    e.run_end = run_end;
+    e.run = k;
+    e.pad = 0;
+    dir[d][b] = e;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total, const RouteDev& ws,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(route_build_kernel, dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp, total, ws);
+  const int64_t lds = 4 * (3 * static_cast<int64_t>(n_slots) + static_cast<int64_t>(cp) * cp);
+  if (lds <= kBuildLdsBytes)
+    hipLaunchKernelGGL(route_build_kernel<true>, dim3(1), dim3(kBuildThreads), static_cast<size_t>(lds), stream, cu,
+                       n_slots, cp, total, ws);
+  else
+    hipLaunchKernelGGL(route_build_kernel<false>, dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp, total,
+                       ws);
   return hipGetLastError();
 }
 
 hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream) {
   const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
   if (n_blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_index_kernel, dim3((n_blocks + 255) / 256), dim3(256), 0, stream, ws, n_blocks, total);
+  hipLaunchKernelGGL(route_index_kernel, dim3((n_blocks + kIndexThreads - 1) / kIndexThreads), dim3(kIndexThreads), 0,
+                     stream, ws, n_blocks, total);
   return hipGetLastError();
 }
 

@@ -80,7 +80,7 @@ typedef struct thd_route thd_route;   /* opaque; owns one device workspace */
  * max_cp <= THD_MAX_CP, max_tokens <= INT32_MAX).  The workspace lives on the
  * current device: (2*max_cp*max_slots + max_cp) runs in each of two orders
  * (8 B each), a max_cp^2 split matrix, two row directories of
- * ceil(max_tokens/16) + 1 entries of 16 B, 2*max_slots int32 of scratch and a
+ * ceil(max_tokens/16) + 1 entries of 16 B, 3*max_slots int32 of scratch and a
  * 64-byte header.  *out (host) receives the handle.  The only call that
  * allocates device memory.  Returns THD_OK, THD_ERR_ARG or THD_ERR_HIP.
  */

@@ -205,3 +205,26 @@ def test_worked_example_on_gpu(thd, golden):
     assert int(status.item()) == 0
     assert mask[0].cpu().numpy().tolist() == [int(v) for v in g["valid_mask"]]
     assert int(mask[0].sum().item()) == int(g["valid_total"][0])
+
+
+# ---- the slow paths of the route build: global scratch instead of LDS, and
+#      directory windows with more runs than the kernel stages in LDS ----
+
+@pytest.mark.parametrize("seed,cp,docs,max_chunk,n_empty", [
+    (200, 2, 7000, 3, 1200),      # 2*n_slots + cp^2 above the LDS budget
+    (201, 128, 5, 3, 2),          # cp^2 above the LDS budget
+    (202, 2, 3000, 1, 0),         # 4-token documents: thousands of runs per 4096-row window
+    (203, 3, 2500, 1, 40),
+])
+def test_route_build_slow_paths(thd, seed, cp, docs, max_chunk, n_empty):
+    import torch
+    w = W.random_packed(seed, cp, docs, max_chunk, n_empty, row_shape=(20,), row_dtype="uint8")
+    cu, total = w.cu_padded, w.total
+    say("slow path", seed, cp, "slots", w.n_slots, "T", total)
+    route = build(thd, cu, cp, total)
+    check_route_matches_oracle(route, cu, cp, total)
+    x = torch.from_numpy(w.rows_host()).cuda()
+    for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+        out = route.swap(x, d)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), O.swap_rows(w.rows_host(), cu, cp, total, direction)), direction
