@@ -144,11 +144,14 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
 
   // Launch shape.  Measured on MI355X: the swap streams best when each
   // workgroup copies about one row -- 4 KiB tiles of 128 threads for rows
-  // under 8 KiB, one row per 512-thread workgroup in XCD-grouped order for
-  // rows of 8 KiB and more.  Every field can be overridden for sweeps.
+  // under 8 KiB; one row per workgroup in XCD-grouped order for rows of 8 KiB
+  // and more, 512 threads up to 4 GiB per buffer and 256 beyond (an empirical
+  // split: 256 wins by ~2 % on the 16 GiB 1M-token batch, 512 by ~1-2 % on
+  // 1-2 GiB batches).  Every field can be overridden for sweeps.
   const bool big_rows = unit == 16 && row_bytes >= 8192;
+  const bool huge = static_cast<int64_t>(total) * row_bytes >= (int64_t{4} << 30);
   const int64_t tile_bytes = cfg.tile_bytes > 0 ? cfg.tile_bytes : (big_rows ? row_bytes : (unit == 16 ? 4096 : 8192));
-  int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (big_rows ? 512 : 128) : 256);
+  int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (big_rows ? (huge ? 256 : 512) : 128) : 256);
   const bool xcd = cfg.tile_order == 2 || (cfg.tile_order == 0 && big_rows);
 
   int64_t tile_rows = (tile_bytes + row_bytes - 1) / row_bytes;
