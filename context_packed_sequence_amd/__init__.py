@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     THD_ERR_REAL_GT_PADDED,
     THD_ERR_SHAPE,
     THD_IDENTITY,
+    THD_MAX_BATCH,
     THD_MAX_CP,
     THD_MAX_SHIFT,
     THD_OK,
@@ -37,6 +38,7 @@ from .binding import (  # noqa: F401
     ThdError,
     thd_build_route,
     thd_roll_labels,
+    thd_roll_labels_zigzag,
     thd_route_copy_out,
     thd_route_create,
     thd_route_destroy,
@@ -44,6 +46,7 @@ from .binding import (  # noqa: F401
     thd_route_status,
     thd_strerror,
     thd_swap,
+    thd_swap_batch,
     thd_swap_tuning,
 )
 
@@ -98,6 +101,32 @@ class Route:
         row_bytes = x.element_size() * (x.numel() // rows if rows else 1)
         code = thd_swap(self.handle, direction, x, out, rows, max(row_bytes, 1), stream)
         return x if code == THD_IDENTITY else out
+
+    def swap_many(self, xs, direction: int, outs=None, stream=None):
+        """Swap several tensors (same token count) in one launch; returns the
+        outputs, or the inputs themselves when the route is the identity."""
+        import torch
+        if outs is None:
+            outs = [torch.empty_like(x, memory_format=torch.contiguous_format) for x in xs]
+        rows = xs[0].shape[0]
+        row_bytes = [max(1, x.element_size() * (x.numel() // rows if rows else 1)) for x in xs]
+        code = thd_swap_batch(self.handle, direction, xs, outs, row_bytes, rows, stream)
+        return list(xs) if code == THD_IDENTITY else outs
+
+    def roll_labels_zigzag(self, ids, cu_seqlens_padded, cu_seqlens=None, max_shift: int = 1, fill: int = 0,
+                           stream=None):
+        """Label shift / MTP roll / valid mask written in this route's zigzag
+        order: shifted [max_shift, T] int64, mask [max_shift + 1, T] uint8,
+        status int32 [1]."""
+        import torch
+        total = int(ids.numel())
+        shifted = torch.empty((max_shift, total), dtype=torch.int64, device=ids.device)
+        mask = torch.empty((max_shift + 1, total), dtype=torch.uint8, device=ids.device)
+        status = torch.empty(1, dtype=torch.int32, device=ids.device)
+        n_slots = int(cu_seqlens_padded.numel()) - 1
+        thd_roll_labels_zigzag(self.handle, ids, cu_seqlens_padded, cu_seqlens, n_slots, total, max_shift, fill,
+                               shifted, mask, status, stream)
+        return shifted, mask, status
 
     def status(self, stream=None) -> int:
         return thd_route_status(self.handle, stream)

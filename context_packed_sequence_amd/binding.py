@@ -42,10 +42,12 @@ THD_ZIGZAG_TO_CONTIGUOUS = 0
 THD_CONTIGUOUS_TO_ZIGZAG = 1
 THD_MAX_CP = 1024
 THD_MAX_SHIFT = 8
+THD_MAX_BATCH = 16
 
 EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",
     "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_swap_tuning", "thd_strerror",
+    "thd_swap_batch", "thd_roll_labels_zigzag",
 )
 
 
@@ -58,7 +60,7 @@ class ThdError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m context_packed_sequence_amd.build_lib` "
+            f"{LIB_PATH} is not built; run `python context_packed_sequence_amd/build_lib.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     c_i32, c_i64, c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -74,6 +76,10 @@ def _load() -> ctypes.CDLL:
                                           ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]),
         "thd_swap_tuning": (ctypes.c_int, [c_i64, c_i32, c_i32, c_i32, c_i32]),
         "thd_strerror": (ctypes.c_char_p, [c_i32]),
+        "thd_swap_batch": (ctypes.c_int, [c_p, c_i32, c_i32, ctypes.POINTER(c_p), ctypes.POINTER(c_p),
+                                          ctypes.POINTER(c_i64), c_i64, c_p]),
+        "thd_roll_labels_zigzag": (ctypes.c_int, [c_p, c_p, c_p, c_p, c_i32, c_i64, c_i32, c_i64, c_p, c_p, c_p,
+                                                  c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -149,6 +155,22 @@ def thd_roll_labels(ids, cu_seqlens_padded, cu_seqlens, n_slots: int, total_toke
     return _check(_lib.thd_roll_labels(_ptr(ids), _ptr(cu_seqlens_padded), _ptr(cu_seqlens), n_slots,
                                        total_tokens, max_shift, fill, _ptr(shifted), _ptr(mask), _ptr(status),
                                        _stream(stream)), "thd_roll_labels")
+
+
+def thd_swap_batch(route: int, direction: int, ins, outs, row_bytes, rows: int, stream=None) -> int:
+    n = len(ins)
+    arr_in = (ctypes.c_void_p * n)(*[_ptr(t) for t in ins])
+    arr_out = (ctypes.c_void_p * n)(*[_ptr(t) for t in outs])
+    arr_rb = (ctypes.c_int64 * n)(*[int(b) for b in row_bytes])
+    return _check(_lib.thd_swap_batch(route, direction, n, arr_in, arr_out, arr_rb, rows, _stream(stream)),
+                  "thd_swap_batch")
+
+
+def thd_roll_labels_zigzag(route: int, ids, cu_seqlens_padded, cu_seqlens, n_slots: int, total_tokens: int,
+                           max_shift: int, fill: int, shifted, mask, status, stream=None) -> int:
+    return _check(_lib.thd_roll_labels_zigzag(route, _ptr(ids), _ptr(cu_seqlens_padded), _ptr(cu_seqlens),
+                                              n_slots, total_tokens, max_shift, fill, _ptr(shifted), _ptr(mask),
+                                              _ptr(status), _stream(stream)), "thd_roll_labels_zigzag")
 
 
 def thd_route_status(route: int, stream=None) -> int:

@@ -1,7 +1,10 @@
 """Build libthdcp.so in-tree with hipcc for gfx950.
 
-    python -m context_packed_sequence_amd.build_lib          # build
-    python -m context_packed_sequence_amd.build_lib --asm    # also keep gfx950 assembly under _build/
+    python context_packed_sequence_amd/build_lib.py          # build
+    python context_packed_sequence_amd/build_lib.py --asm    # also keep gfx950 assembly under _build/
+
+Run it as a file (or through __graft_entry__.build()), not as a module of the
+package: importing the package loads the library, which may not exist yet.
 
 Every source is compiled on each call (the build check compiles even when a
 library is already present).  Objects go to ``_build/`` beside the package; the

@@ -50,6 +50,20 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+int check_roll_args(const int64_t* ids, const int32_t* cu_pad, int32_t n_slots, int64_t total, int32_t max_shift,
+                    const int64_t* shifted, const uint8_t* mask, const int32_t* status) {
+  if (!cu_pad || n_slots < 0 || total < 0 || total > INT32_MAX) return THD_ERR_ARG;
+  if (max_shift < 1 || max_shift > THD_MAX_SHIFT) return THD_ERR_ARG;
+  if (total > 0 && (!ids || !shifted || !mask)) return THD_ERR_ARG;
+  const int64_t t = total;
+  if (overlaps(shifted, t * max_shift * 8, ids, t * 8) || overlaps(mask, t * (max_shift + 1), ids, t * 8) ||
+      overlaps(mask, t * (max_shift + 1), shifted, t * max_shift * 8))
+    return THD_ERR_ALIAS;
+  if (status && (overlaps(status, 4, shifted, t * max_shift * 8) || overlaps(status, 4, mask, t * (max_shift + 1))))
+    return THD_ERR_ALIAS;
+  return THD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,17 +194,59 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
 int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const int32_t* cu_seqlens, int32_t n_slots,
                     int64_t total_tokens, int32_t max_shift, int64_t fill, int64_t* shifted, uint8_t* mask,
                     int32_t* status, void* stream) {
-  if (!cu_seqlens_padded || n_slots < 0 || total_tokens < 0 || total_tokens > INT32_MAX) return THD_ERR_ARG;
-  if (max_shift < 1 || max_shift > THD_MAX_SHIFT) return THD_ERR_ARG;
-  if (total_tokens > 0 && (!ids || !shifted || !mask)) return THD_ERR_ARG;
-  const int64_t t = total_tokens;
-  if (overlaps(shifted, t * max_shift * 8, ids, t * 8) || overlaps(mask, t * (max_shift + 1), ids, t * 8) ||
-      overlaps(mask, t * (max_shift + 1), shifted, t * max_shift * 8))
-    return THD_ERR_ALIAS;
-  if (status && (overlaps(status, 4, shifted, t * max_shift * 8) || overlaps(status, 4, mask, t * (max_shift + 1))))
-    return THD_ERR_ALIAS;
+  const int rc = check_roll_args(ids, cu_seqlens_padded, n_slots, total_tokens, max_shift, shifted, mask, status);
+  if (rc != THD_OK) return rc;
   if (thdcp::launch_roll(ids, cu_seqlens_padded, cu_seqlens, n_slots, static_cast<int32_t>(total_tokens), max_shift,
-                         fill, shifted, mask, status, as_stream(stream)) != hipSuccess)
+                         fill, shifted, mask, status, nullptr, as_stream(stream)) != hipSuccess)
+    return THD_ERR_HIP;
+  return THD_OK;
+}
+
+int thd_roll_labels_zigzag(const thd_route* route, const int64_t* ids, const int32_t* cu_seqlens_padded,
+                           const int32_t* cu_seqlens, int32_t n_slots, int64_t total_tokens, int32_t max_shift,
+                           int64_t fill, int64_t* shifted, uint8_t* mask, int32_t* status, void* stream) {
+  if (!route) return THD_ERR_ARG;
+  if (!route->built) return THD_ERR_NOT_BUILT;
+  if (total_tokens != route->total) return THD_ERR_SHAPE;
+  if (route->cp == 1 || total_tokens == 0)
+    return thd_roll_labels(ids, cu_seqlens_padded, cu_seqlens, n_slots, total_tokens, max_shift, fill, shifted, mask,
+                           status, stream);
+  const int rc = check_roll_args(ids, cu_seqlens_padded, n_slots, total_tokens, max_shift, shifted, mask, status);
+  if (rc != THD_OK) return rc;
+  if (!on_route_device(route)) return THD_ERR_DEVICE;
+  const thdcp::RollRoute rt{route->dev.hdr, route->dev.runs_dst, route->dev.dir_dst};
+  if (thdcp::launch_roll(ids, cu_seqlens_padded, cu_seqlens, n_slots, static_cast<int32_t>(total_tokens), max_shift,
+                         fill, shifted, mask, status, &rt, as_stream(stream)) != hipSuccess)
+    return THD_ERR_HIP;
+  return THD_OK;
+}
+
+int thd_swap_batch(const thd_route* route, int32_t direction, int32_t n_tensors, const void* const* ins,
+                   void* const* outs, const int64_t* row_bytes, int64_t rows, void* stream) {
+  if (!route || rows < 0 || n_tensors < 1 || n_tensors > THD_MAX_BATCH || !ins || !outs || !row_bytes)
+    return THD_ERR_ARG;
+  if (direction != THD_ZIGZAG_TO_CONTIGUOUS && direction != THD_CONTIGUOUS_TO_ZIGZAG) return THD_ERR_DIRECTION;
+  if (!route->built) return THD_ERR_NOT_BUILT;
+  if (rows != route->total) return THD_ERR_SHAPE;
+  for (int32_t i = 0; i < n_tensors; ++i)
+    if (row_bytes[i] < 1 || (rows > 0 && row_bytes[i] > INT64_MAX / rows)) return THD_ERR_ARG;
+  if (route->cp == 1 || rows == 0) return THD_IDENTITY;
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    if (!ins[i] || !outs[i]) return THD_ERR_ARG;
+    const int64_t bi = rows * row_bytes[i];
+    for (int32_t j = 0; j < n_tensors; ++j) {
+      const int64_t bj = rows * row_bytes[j];
+      if (overlaps(outs[i], bi, ins[j], bj)) return THD_ERR_ALIAS;
+      if (j != i && overlaps(outs[i], bi, outs[j], bj)) return THD_ERR_ALIAS;
+    }
+  }
+  if (!on_route_device(route)) return THD_ERR_DEVICE;
+  const bool z2c = direction == THD_ZIGZAG_TO_CONTIGUOUS;
+  const RunPair* runs = z2c ? route->dev.runs_dst : route->dev.runs_src;
+  const thdcp::DirEntry* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
+  const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
+  if (thdcp::launch_swap_batch(route->dev.hdr, runs, word, dir, n_tensors, ins, outs, row_bytes,
+                               static_cast<int32_t>(rows), as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;
   return THD_OK;
 }

@@ -72,9 +72,21 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
                        const void* in, void* out, int32_t total, int64_t row_bytes,
                        const SwapLaunch& cfg, hipStream_t stream);
 
+hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
+                             int32_t n, const void* const* ins, void* const* outs, const int64_t* row_bytes,
+                             int32_t total, hipStream_t stream);
+
+// Token-order runs of a route, for writing the roll's outputs in zigzag order.
+struct RollRoute {
+  const int32_t* hdr;
+  const RunPair* runs;
+  const DirEntry* dir;
+};
+
 hipError_t launch_roll(const int64_t* ids, const int32_t* cu_pad, const int32_t* cu_real,
                        int32_t n_slots, int32_t total, int32_t max_shift, int64_t fill,
-                       int64_t* shifted, uint8_t* mask, int32_t* status, hipStream_t stream);
+                       int64_t* shifted, uint8_t* mask, int32_t* status, const RollRoute* route,
+                       hipStream_t stream);
 
 // Severity of a validation failure: larger wins; 0 = no failure.
 __host__ __device__ inline int32_t severity_to_code(int sev) {

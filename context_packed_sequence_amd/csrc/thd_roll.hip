@@ -26,13 +26,26 @@ namespace {
 constexpr int kRollThreads = 256;
 constexpr int kRollLdsSlots = 4096;  // boundaries staged in LDS (dynamic, 8 B per slot, <= 32 KiB)
 
-template <bool kLds>
+// Zigzag row of token t from a route's token-order runs (out = token, in =
+// zigzag row) and their directory; every access stays in the run table.
+__device__ __forceinline__ int32_t zigzag_row_of(const RollRoute& rt, int32_t n_runs, int32_t t) {
+  const DirEntry e = rt.dir[t >> kDirShift];
+  if (t < e.run_end) return e.in + (t & (kDirBlock - 1));
+  int32_t k = e.run + 1;
+  while (k + 1 < n_runs && rt.runs[k + 1].out <= t) ++k;
+  k = min(k, n_runs - 1);
+  const RunPair r = rt.runs[k];
+  return r.in + (t - r.out);
+}
+
+template <bool kLds, bool kRouted>
 __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __restrict__ ids,
                                                             const int32_t* __restrict__ cu_pad,
                                                             const int32_t* __restrict__ cu_real, int32_t n_slots,
                                                             int32_t total, int32_t max_shift, int64_t fill,
                                                             int64_t* __restrict__ shifted,
-                                                            uint8_t* __restrict__ mask, int32_t* __restrict__ status) {
+                                                            uint8_t* __restrict__ mask, int32_t* __restrict__ status,
+                                                            RollRoute rt) {
   extern __shared__ int32_t s_cu[];                   // kLds: [n_slots + 1] padded, then [n_slots] real lengths
   int32_t* s_pad = s_cu;
   int32_t* s_len = s_cu + (n_slots + 1);
@@ -62,7 +75,13 @@ __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __res
   }
   if (sev) atomicMax(&s_sev, sev);
   __syncthreads();
-  const int32_t code = severity_to_code(s_sev);
+  int32_t code = severity_to_code(s_sev);
+  int32_t n_runs = 0;
+  if constexpr (kRouted) {
+    const int32_t route_status = rt.hdr[kHdrStatus];
+    if (route_status != THD_OK) code = route_status;  // a failed route build comes first
+    n_runs = rt.hdr[kHdrRunsDst];
+  }
   if (status && blockIdx.x == 0 && tid == 0) *status = code;
   if (code != THD_OK) return;
 
@@ -87,11 +106,12 @@ __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __res
   else real_len = cu_real ? static_cast<int64_t>(cu_real[lo + 1]) - cu_real[lo]
                           : static_cast<int64_t>(cu_pad[lo + 1]) - cu_pad[lo];
   const int64_t e = static_cast<int64_t>(kLds ? s_pad[lo] : cu_pad[lo]) + real_len;
-  mask[t] = t < e ? 1 : 0;
+  const int64_t row = kRouted ? zigzag_row_of(rt, n_runs, static_cast<int32_t>(t)) : t;
+  mask[row] = t < e ? 1 : 0;
   for (int j = 1; j <= max_shift; ++j) {
     const bool ok = t + j < e;
-    shifted[static_cast<int64_t>(j - 1) * total + t] = ok ? s_ids[tid + j] : fill;
-    mask[static_cast<int64_t>(j) * total + t] = ok ? 1 : 0;
+    shifted[static_cast<int64_t>(j - 1) * total + row] = ok ? s_ids[tid + j] : fill;
+    mask[static_cast<int64_t>(j) * total + row] = ok ? 1 : 0;
   }
 }
 
@@ -99,15 +119,23 @@ __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __res
 
 hipError_t launch_roll(const int64_t* ids, const int32_t* cu_pad, const int32_t* cu_real, int32_t n_slots,
                        int32_t total, int32_t max_shift, int64_t fill, int64_t* shifted, uint8_t* mask,
-                       int32_t* status, hipStream_t stream) {
+                       int32_t* status, const RollRoute* route, hipStream_t stream) {
   const int64_t blocks64 = total > 0 ? (static_cast<int64_t>(total) + kRollThreads - 1) / kRollThreads : 1;
   const dim3 grid(static_cast<unsigned>(blocks64));
-  if (n_slots + 1 <= kRollLdsSlots)
-    hipLaunchKernelGGL(roll_kernel<true>, grid, dim3(kRollThreads), static_cast<size_t>(2 * n_slots + 1) * 4, stream,
-                       ids, cu_pad, cu_real, n_slots, total, max_shift, fill, shifted, mask, status);
-  else
-    hipLaunchKernelGGL(roll_kernel<false>, grid, dim3(kRollThreads), 0, stream, ids, cu_pad, cu_real, n_slots, total,
-                       max_shift, fill, shifted, mask, status);
+  const RollRoute rt = route ? *route : RollRoute{nullptr, nullptr, nullptr};
+  const bool lds = n_slots + 1 <= kRollLdsSlots;
+  const size_t lds_bytes = lds ? static_cast<size_t>(2 * n_slots + 1) * 4 : 0;
+#define THD_ROLL(L, R)                                                                                             \
+  hipLaunchKernelGGL((roll_kernel<L, R>), grid, dim3(kRollThreads), lds_bytes, stream, ids, cu_pad, cu_real,      \
+                     n_slots, total, max_shift, fill, shifted, mask, status, rt)
+  if (lds) {
+    if (route) THD_ROLL(true, true);
+    else THD_ROLL(true, false);
+  } else {
+    if (route) THD_ROLL(false, true);
+    else THD_ROLL(false, false);
+  }
+#undef THD_ROLL
   return hipGetLastError();
 }
 

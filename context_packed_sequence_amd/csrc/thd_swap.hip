@@ -20,6 +20,8 @@
 // small workgroups keep the set of rows being copied at any moment inside a
 // narrow, sliding address window, which is what lets a copy approach the HBM
 // roofline; loads and stores are non-temporal because nothing is reused.
+#include <climits>
+
 #include "thd_internal.h"
 
 namespace thdcp {
@@ -54,6 +56,125 @@ __device__ __forceinline__ void copy_span(const U* __restrict__ src, U* __restri
   for (int64_t i = base + tid; i < n; i += BLOCK) store_unit<NT>(dst + i, load_unit<NT>(src + i));
 }
 
+// One tile of output rows [r0, r1): find the run holding r0 from the
+// directory (one 16-byte load covers the usual case where no run starts
+// between the directory row, a multiple of 16, and r0), then copy run piece by
+// run piece.  Every access stays inside the run table and inside [0, total)
+// rows of both buffers.
+template <typename U, int BLOCK, int UNROLL, bool NT>
+__device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
+                                          int32_t n_runs, const unsigned char* __restrict__ in,
+                                          unsigned char* __restrict__ out, int32_t total, int64_t row_bytes,
+                                          int32_t r0, int32_t r1) {
+  const DirEntry e = dir[r0 >> kDirShift];
+  int32_t k, in_row, run_end;
+  if (r0 < e.run_end) {
+    k = e.run;
+    in_row = e.in + (r0 & (kDirBlock - 1));
+    run_end = e.run_end;
+  } else {
+    k = e.run + 1;
+    while (k + 1 < n_runs && runs[k + 1].out <= r0) ++k;
+    if (k >= n_runs) return;
+    const RunPair run = runs[k];
+    if (run.out > r0) return;
+    in_row = run.in + (r0 - run.out);
+    run_end = (k + 1 < n_runs) ? runs[k + 1].out : total;
+  }
+  while (true) {
+    const int32_t piece_end = min(r1, run_end);
+    const U* src = reinterpret_cast<const U*>(in + static_cast<int64_t>(in_row) * row_bytes);
+    U* dst = reinterpret_cast<U*>(out + static_cast<int64_t>(r0) * row_bytes);
+    const int64_t n_units = static_cast<int64_t>(piece_end - r0) * row_bytes / static_cast<int64_t>(sizeof(U));
+    copy_span<U, BLOCK, UNROLL, NT>(src, dst, n_units);
+    r0 = piece_end;
+    if (r0 >= r1 || ++k >= n_runs) break;
+    const RunPair run = runs[k];
+    if (run.out != r0) break;  // runs tile the output rows; never trust anything else
+    in_row = run.in;
+    run_end = (k + 1 < n_runs) ? runs[k + 1].out : total;
+  }
+}
+
+// Small rows (row_bytes equal to the copy unit, at most 16 B: token ids,
+// labels, masks, position ids): copying run piece by run piece would leave
+// most lanes idle on short pieces, so the tile's runs are staged in LDS and
+// every thread looks up the run of each of its rows there, then moves the
+// row with one load and one store.  Consecutive lanes take consecutive
+// output rows, so the stores are fully coalesced, and so are the loads inside
+// a run.  Tiles whose rows cross more than kSmallStage runs fall back to the
+// piecewise copy.
+constexpr int kSmallRowsPerThread = 4;
+constexpr int kSmallStage = 512;
+
+template <typename U, int BLOCK, bool NT>
+__device__ __forceinline__ void swap_tile_small(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
+                                                int32_t n_runs, const unsigned char* __restrict__ in8,
+                                                unsigned char* __restrict__ out8, int32_t total, int32_t r0,
+                                                int32_t r1, RunPair* s_runs, int32_t* s_k) {
+  const int tid = threadIdx.x;
+  if (tid < 2) {  // run holding the first row and run holding the last row of the tile
+    const int32_t row = tid == 0 ? r0 : r1 - 1;
+    const DirEntry e = dir[row >> kDirShift];
+    int32_t k = e.run;
+    if (row >= e.run_end) {
+      k = e.run + 1;
+      while (k + 1 < n_runs && runs[k + 1].out <= row) ++k;
+    }
+    s_k[tid] = min(k, n_runs - 1);
+  }
+  __syncthreads();
+  const int32_t k0 = s_k[0];
+  const int32_t cnt = s_k[1] - k0 + 1;
+  if (cnt <= kSmallStage) {
+    for (int i = tid; i < cnt; i += BLOCK) s_runs[i] = runs[k0 + i];
+    __syncthreads();
+    const U* in = reinterpret_cast<const U*>(in8);
+    U* out = reinterpret_cast<U*>(out8);
+    U v[kSmallRowsPerThread];
+#pragma unroll
+    for (int m = 0; m < kSmallRowsPerThread; ++m) {
+      const int32_t r = r0 + m * BLOCK + tid;
+      if (r < r1) {
+        int32_t lo = 0, hi = cnt;  // s_runs[lo].out <= r
+        while (hi - lo > 1) {
+          const int32_t mid = (lo + hi) >> 1;
+          if (s_runs[mid].out <= r) lo = mid;
+          else hi = mid;
+        }
+        v[m] = load_unit<NT>(in + (s_runs[lo].in + (r - s_runs[lo].out)));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kSmallRowsPerThread; ++m) {
+      const int32_t r = r0 + m * BLOCK + tid;
+      if (r < r1) store_unit<NT>(out + r, v[m]);
+    }
+  } else {
+    swap_tile<U, BLOCK, 8, NT>(runs, dir, n_runs, in8, out8, total, static_cast<int64_t>(sizeof(U)), r0, r1);
+  }
+  __syncthreads();  // the next tile reuses s_runs and s_k
+}
+
+template <typename U, int BLOCK, bool NT>
+__global__ __launch_bounds__(BLOCK) void swap_small_kernel(const int32_t* __restrict__ hdr, int runs_word,
+                                                           const RunPair* __restrict__ runs,
+                                                           const DirEntry* __restrict__ dir,
+                                                           const unsigned char* __restrict__ in,
+                                                           unsigned char* __restrict__ out, int32_t total,
+                                                           int32_t n_tiles) {
+  __shared__ RunPair s_runs[kSmallStage];
+  __shared__ int32_t s_k[2];
+  if (hdr[kHdrStatus] != THD_OK) return;
+  const int32_t n_runs = hdr[runs_word];
+  constexpr int32_t kTileRows = BLOCK * kSmallRowsPerThread;
+  for (int32_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int32_t r0 = tile * kTileRows;
+    const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + kTileRows));
+    swap_tile_small<U, BLOCK, NT>(runs, dir, n_runs, in, out, total, r0, r1, s_runs, s_k);
+  }
+}
+
 // Tile order.  Natural: workgroup b copies tile b.  XCD-grouped: the chip
 // hands workgroup b to XCD b mod 8, so tile (b mod 8) * ceil(n/8) + b / 8 gives
 // every XCD one contiguous eighth of the output, streamed front to back.
@@ -73,39 +194,74 @@ __global__ __launch_bounds__(BLOCK) void swap_kernel(const int32_t* __restrict__
   for (int32_t slot = blockIdx.x; slot < n_slots; slot += gridDim.x) {
     const int32_t tile = XCD ? (slot % kXcds) * per_xcd + slot / kXcds : slot;
     if (tile >= n_tiles) continue;
-    int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(tile) * tile_rows);
+    const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(tile) * tile_rows);
     const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + tile_rows));
-    // First piece: one directory load covers the usual case where no run
-    // starts between the directory row (a multiple of 16) and r0.
-    const DirEntry e = dir[r0 >> kDirShift];
-    int32_t k, in_row, run_end;
-    if (r0 < e.run_end) {
-      k = e.run;
-      in_row = e.in + (r0 & (kDirBlock - 1));
-      run_end = e.run_end;
-    } else {
-      k = e.run + 1;
-      while (k + 1 < n_runs && runs[k + 1].out <= r0) ++k;
-      if (k >= n_runs) continue;
-      const RunPair run = runs[k];
-      if (run.out > r0) continue;
-      in_row = run.in + (r0 - run.out);
-      run_end = (k + 1 < n_runs) ? runs[k + 1].out : total;
+    swap_tile<U, BLOCK, UNROLL, NT>(runs, dir, n_runs, in, out, total, row_bytes, r0, r1);
+  }
+}
+
+// Several tensors through one route in one launch (the tokens, labels,
+// loss mask, position ids and valid mask of a batch, or the projections of one
+// layer): the launch's tiles are the concatenation of every tensor's tiles,
+// each tensor with its own row size and copy unit.
+struct BatchTensor {
+  const unsigned char* in;
+  unsigned char* out;
+  int64_t row_bytes;
+  int32_t tile_rows;
+  int32_t first_tile;  // index of the tensor's first tile in the launch
+  int32_t unit;        // copy unit in bytes: 16, 8, 4, 2 or 1
+  int32_t pad;
+};
+
+struct BatchArgs {
+  BatchTensor t[THD_MAX_BATCH];
+  int32_t n;
+  int32_t total_tiles;
+};
+
+constexpr int kBatchBlock = 256;
+
+__global__ __launch_bounds__(kBatchBlock) void swap_batch_kernel(const int32_t* __restrict__ hdr, int runs_word,
+                                                                 const RunPair* __restrict__ runs,
+                                                                 const DirEntry* __restrict__ dir, int32_t total,
+                                                                 BatchArgs args) {
+  __shared__ RunPair s_runs[kSmallStage];
+  __shared__ int32_t s_k[2];
+  if (hdr[kHdrStatus] != THD_OK) return;
+  const int32_t n_runs = hdr[runs_word];
+  for (int32_t g = blockIdx.x; g < args.total_tiles; g += gridDim.x) {
+    int i = 0;
+    while (i + 1 < args.n && args.t[i + 1].first_tile <= g) ++i;
+    const BatchTensor bt = args.t[i];
+    const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(g - bt.first_tile) * bt.tile_rows);
+    const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + bt.tile_rows));
+    if (bt.row_bytes == bt.unit) {  // one unit per row: the LDS-staged small-row path
+      switch (bt.unit) {
+        case 16: swap_tile_small<u32x4, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
+        case 8: swap_tile_small<u32x2, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
+        case 4: swap_tile_small<uint32_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
+        case 2: swap_tile_small<uint16_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
+        default: swap_tile_small<uint8_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
+      }
+      continue;
     }
-    while (true) {
-      const int32_t piece_end = min(r1, run_end);
-      const U* src = reinterpret_cast<const U*>(in + static_cast<int64_t>(in_row) * row_bytes);
-      U* dst = reinterpret_cast<U*>(out + static_cast<int64_t>(r0) * row_bytes);
-      const int64_t n_units = static_cast<int64_t>(piece_end - r0) * row_bytes / static_cast<int64_t>(sizeof(U));
-      copy_span<U, BLOCK, UNROLL, NT>(src, dst, n_units);
-      r0 = piece_end;
-      if (r0 >= r1 || ++k >= n_runs) break;
-      const RunPair run = runs[k];
-      if (run.out != r0) break;  // runs tile the output rows; never trust anything else
-      in_row = run.in;
-      run_end = (k + 1 < n_runs) ? runs[k + 1].out : total;
+    switch (bt.unit) {
+      case 16: swap_tile<u32x4, kBatchBlock, 4, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 8: swap_tile<u32x2, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 4: swap_tile<uint32_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 2: swap_tile<uint16_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      default: swap_tile<uint8_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
     }
   }
+}
+
+int copy_unit(int64_t row_bytes, const void* in, const void* out) {
+  const uint64_t align_bits = static_cast<uint64_t>(row_bytes) | reinterpret_cast<uintptr_t>(in) |
+                              reinterpret_cast<uintptr_t>(out);
+  int unit = 16;
+  while (unit > 1 && (align_bits & (unit - 1))) unit >>= 1;
+  return unit;
 }
 
 struct Shape {
@@ -137,10 +293,31 @@ hipError_t launch_typed(const int32_t* hdr, const RunPair* runs, int runs_word, 
 hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir, const void* in,
                        void* out, int32_t total, int64_t row_bytes, const SwapLaunch& cfg, hipStream_t stream) {
   // Widest unit that divides the row size and both base addresses.
-  const uint64_t align_bits = static_cast<uint64_t>(row_bytes) | reinterpret_cast<uintptr_t>(in) |
-                              reinterpret_cast<uintptr_t>(out);
-  int unit = 16;
-  while (unit > 1 && (align_bits & (unit - 1))) unit >>= 1;
+  const int unit = copy_unit(row_bytes, in, out);
+
+  if (row_bytes == unit && cfg.tile_bytes == 0 && cfg.block_threads == 0) {
+    constexpr int kBlock = 256;
+    const int64_t tiles = (static_cast<int64_t>(total) + kBlock * kSmallRowsPerThread - 1) /
+                          (kBlock * kSmallRowsPerThread);
+    int32_t grid = static_cast<int32_t>(tiles);
+    if (cfg.max_workgroups > 0 && grid > cfg.max_workgroups) grid = cfg.max_workgroups;
+    if (grid <= 0) return hipSuccess;
+    const auto* i8 = static_cast<const unsigned char*>(in);
+    auto* o8 = static_cast<unsigned char*>(out);
+    const int32_t nt_ = static_cast<int32_t>(tiles);
+#define THD_SMALL(U_)                                                                                               \
+  hipLaunchKernelGGL((swap_small_kernel<U_, kBlock, true>), dim3(grid), dim3(kBlock), 0, stream, hdr, runs_word, runs, \
+                     dir, i8, o8, total, nt_)
+    switch (unit) {
+      case 16: THD_SMALL(u32x4); break;
+      case 8: THD_SMALL(u32x2); break;
+      case 4: THD_SMALL(uint32_t); break;
+      case 2: THD_SMALL(uint16_t); break;
+      default: THD_SMALL(uint8_t); break;
+    }
+#undef THD_SMALL
+    return hipGetLastError();
+  }
 
   // Launch shape.  Measured on MI355X: the swap streams best when each
   // workgroup copies about one row -- 4 KiB tiles of 128 threads for rows
@@ -180,6 +357,35 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
     default: return launch_typed<uint8_t, 256, 8>(THD_SWAP_ARGS);
   }
 #undef THD_SWAP_ARGS
+}
+
+hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
+                             int32_t n, const void* const* ins, void* const* outs, const int64_t* row_bytes,
+                             int32_t total, hipStream_t stream) {
+  BatchArgs args{};
+  args.n = n;
+  int64_t tiles = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int unit = copy_unit(row_bytes[i], ins[i], outs[i]);
+    const int64_t tile_bytes = unit == 16 ? 4096 : 8192;
+    int64_t tile_rows = row_bytes[i] == unit ? kBatchBlock * kSmallRowsPerThread
+                                             : (tile_bytes + row_bytes[i] - 1) / row_bytes[i];
+    if (tile_rows < 1) tile_rows = 1;
+    if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
+    args.t[i].in = static_cast<const unsigned char*>(ins[i]);
+    args.t[i].out = static_cast<unsigned char*>(outs[i]);
+    args.t[i].row_bytes = row_bytes[i];
+    args.t[i].tile_rows = static_cast<int32_t>(tile_rows);
+    args.t[i].first_tile = static_cast<int32_t>(tiles);
+    args.t[i].unit = unit;
+    tiles += (total + tile_rows - 1) / tile_rows;
+  }
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  args.total_tiles = static_cast<int32_t>(tiles);
+  hipLaunchKernelGGL(swap_batch_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kBatchBlock), 0, stream, hdr,
+                     runs_word, runs, dir, total, args);
+  return hipGetLastError();
 }
 
 }  // namespace thdcp

@@ -71,6 +71,7 @@ extern "C" {
 /* ---- limits -------------------------------------------------------------- */
 #define THD_MAX_CP        1024
 #define THD_MAX_SHIFT     8
+#define THD_MAX_BATCH     16
 
 typedef struct thd_route thd_route;   /* opaque; owns one device workspace */
 
@@ -139,6 +140,22 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
              int64_t rows, int64_t row_bytes, void* stream);
 
 /*
+ * thd_swap_batch -- thd_swap for n_tensors tensors (1..THD_MAX_BATCH) in one
+ * kernel launch: the tokens, labels, loss mask, position ids and valid mask
+ * of a packed batch all take the same route ("Packed Sequence 与上下文并行"
+ * §2.4 slices every per-token stream with one index), as do the several
+ * activations of one layer.
+ *
+ * ins, outs, row_bytes: host arrays of n_tensors entries; ins[i] and outs[i]
+ * are device buffers of rows x row_bytes[i] bytes, row-major, token dimension
+ * outermost.  No output may overlap any input or any other output
+ * (THD_ERR_ALIAS).  Other rules as thd_swap; THD_IDENTITY when the route is
+ * the identity (nothing written, callers keep their inputs).
+ */
+int thd_swap_batch(const thd_route* route, int32_t direction, int32_t n_tensors, const void* const* ins,
+                   void* const* outs, const int64_t* row_bytes, int64_t rows, void* stream);
+
+/*
  * thd_roll_labels -- document-aware label shift, MTP roll and valid-token mask
  * in one pass ("Packed Sequence 与上下文并行" §1.3, §1.6, §2.2).
  *
@@ -167,6 +184,23 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
 int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const int32_t* cu_seqlens,
                     int32_t n_slots, int64_t total_tokens, int32_t max_shift, int64_t fill,
                     int64_t* shifted, uint8_t* mask, int32_t* status, void* stream);
+
+/*
+ * thd_roll_labels_zigzag -- thd_roll_labels with its outputs written in the
+ * emulated zigzag layout of `route`, i.e. the roll followed by the c->z slice
+ * of every output stream, in one pass: row t of each natural-order stream
+ * lands on the zigzag row that holds token t ("Packed Sequence 与上下文并行"
+ * §2.2 rolls labels at pack time and §2.4 slices them with the tokens).
+ *
+ * The route must have been built from the same cu_seqlens_padded and
+ * total_tokens (THD_ERR_SHAPE if total_tokens differs, THD_ERR_NOT_BUILT if
+ * never built).  Identity route (cp_size 1): same as thd_roll_labels.  If the
+ * route's status is an error, that code is written to `status` and nothing
+ * else is written.  Other arguments, errors and outputs as thd_roll_labels.
+ */
+int thd_roll_labels_zigzag(const thd_route* route, const int64_t* ids, const int32_t* cu_seqlens_padded,
+                           const int32_t* cu_seqlens, int32_t n_slots, int64_t total_tokens, int32_t max_shift,
+                           int64_t fill, int64_t* shifted, uint8_t* mask, int32_t* status, void* stream);
 
 /*
  * thd_route_status -- SYNC.  Waits for `stream`, then stores the status word

@@ -1,0 +1,243 @@
+"""Multi-tensor swap, roll written in zigzag order, and HIP-graph capture.
+
+* thd_swap_batch moves the per-token streams of a packed batch (token ids,
+  labels, loss mask, position ids, valid mask) and an activation through one
+  route in one launch ("Packed Sequence 与上下文并行" §2.4 slices every key
+  with the same index); each output must equal the oracle's swap of that
+  tensor byte for byte.
+* thd_roll_labels_zigzag must equal the oracle's roll followed by the oracle's
+  c->z swap of every output stream.
+* A HIP graph capturing build + swaps + roll replays to the eager results,
+  and picks up new boundaries written into the captured buffer (the route is
+  a device-resident capture input).
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import dev_i32, dev_i64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def thd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import context_packed_sequence_amd as thd
+    return thd
+
+
+def batch_keys(w, rng):
+    """Per-token streams of a packed batch plus one activation (host arrays)."""
+    t = w.total
+    return {
+        "tokens": w.ids(),
+        "labels": rng.integers(-1, 32000, size=t, dtype=np.int64),
+        "loss_mask": rng.integers(0, 2, size=t, dtype=np.uint8),
+        "position_ids": rng.integers(0, 65536, size=t, dtype=np.int64),
+        "valid_mask": rng.integers(0, 2, size=t, dtype=np.uint8),
+        "fp32_pair": rng.standard_normal((t, 2), dtype=np.float32),
+        "hidden": w.rows_host().view(np.int16),      # bf16 bit patterns
+    }
+
+
+@pytest.mark.parametrize("seed,cp,docs,max_chunk,n_empty", [
+    (0, 2, 9, 40, 0), (1, 4, 40, 64, 3), (2, 8, 25, 20, 8), (3, 3, 200, 6, 30), (4, 16, 12, 9, 4)])
+def test_swap_batch_matches_per_tensor_oracle(thd, seed, cp, docs, max_chunk, n_empty):
+    import torch
+    w = W.random_packed(seed, cp, docs, max_chunk, n_empty, row_shape=(2, 24))
+    cu, total = w.cu_padded, w.total
+    say("batch", seed, cp, "T", total)
+    route = thd.Route(w.n_slots, cp, total)
+    route.build(dev_i32(cu), cp, total)
+    keys = batch_keys(w, np.random.default_rng(seed))
+    xs = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in keys.values()]
+    for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+        outs = route.swap_many(xs, d)
+        torch.cuda.synchronize()
+        for (name, host), out in zip(keys.items(), outs):
+            want = O.swap_rows(host, cu, cp, total, direction)
+            assert np.array_equal(out.cpu().numpy().view(host.dtype), want), (name, direction)
+
+
+def test_swap_batch_full_workload(thd):
+    # The full micro-batch's per-token streams in one launch, plus the guard
+    # that outputs land only where they belong (sentinel around each output).
+    import torch
+    w = W.make("full")
+    cu, total, cp = w.cu_padded, w.total, w.cp
+    route = thd.Route(w.n_slots, cp, total)
+    route.build(dev_i32(cu), cp, total)
+    rng = np.random.default_rng(9)
+    keys = batch_keys(w, rng)
+    keys.pop("hidden")
+    xs = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in keys.values()]
+    pads = []
+    outs = []
+    for x in xs:
+        nbytes = x.numel() * x.element_size()
+        buf = torch.full((nbytes + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+        pads.append(buf)
+        outs.append(buf[128:128 + nbytes].view(x.dtype).view(x.shape))
+    rbs = [x.numel() * x.element_size() // total for x in xs]
+    assert thd.thd_swap_batch(route.handle, thd.C2Z, xs, outs, rbs, total) == thd.THD_OK
+    torch.cuda.synchronize()
+    for (name, host), out, buf in zip(keys.items(), outs, pads):
+        assert np.array_equal(out.cpu().numpy(), O.swap_rows(host, cu, cp, total, "c2z")), name
+        b = buf.cpu().numpy()
+        assert (b[:128] == 0xA5).all() and (b[-128:] == 0xA5).all(), name
+
+
+def test_swap_batch_errors(thd):
+    import torch
+    route = thd.Route(4, 2, 32)
+    route.build(dev_i32([0, 16, 32]), 2, 32)
+    a = torch.zeros(32, 8, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(32, 8, dtype=torch.uint8, device="cuda")
+    c = torch.zeros(32, 4, dtype=torch.uint8, device="cuda")
+    for args, code in [
+        ((route.handle, thd.Z2C, [a, b], [c, c], [8, 8], 32), thd.THD_ERR_ALIAS),       # two outputs overlap
+        ((route.handle, thd.Z2C, [a, b], [b, c], [8, 8], 32), thd.THD_ERR_ALIAS),       # output over an input
+        ((route.handle, 5, [a], [b], [8], 32), thd.THD_ERR_DIRECTION),
+        ((route.handle, thd.Z2C, [a], [b], [8], 16), thd.THD_ERR_SHAPE),
+        ((route.handle, thd.Z2C, [a], [b], [0], 32), thd.THD_ERR_ARG),
+        ((route.handle, thd.Z2C, [a] * 17, [b] * 17, [8] * 17, 32), thd.THD_ERR_ARG),
+    ]:
+        with pytest.raises(thd.ThdError) as e:
+            thd.thd_swap_batch(*args)
+        assert e.value.code == code, args
+
+
+@pytest.mark.parametrize("name", ["tiny", "gdn128k", "full"])
+def test_roll_zigzag_matches_roll_then_slice(thd, name):
+    import torch
+    w = W.make(name)
+    cu, total, cp = w.cu_padded, w.total, w.cp
+    j = max(w.max_shift, 2)
+    route = thd.Route(w.n_slots, cp, total)
+    route.build(dev_i32(cu), cp, total)
+    ids = w.ids()
+    say("roll zigzag", name)
+    shifted, mask, status = route.roll_labels_zigzag(dev_i64(ids), dev_i32(cu), dev_i32(w.cu_real), j, -1)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    want_s, want_m = O.roll_labels(ids, cu, w.cu_real, total, j, -1)
+    for k in range(j):
+        assert np.array_equal(shifted[k].cpu().numpy(), O.swap_rows(want_s[k], cu, cp, total, "c2z")), k
+    for k in range(j + 1):
+        assert np.array_equal(mask[k].cpu().numpy(), O.swap_rows(want_m[k], cu, cp, total, "c2z")), k
+
+
+def test_roll_zigzag_worked_example(thd, golden):
+    # §3.6: each rank's valid mask after the slice, straight from the roll.
+    import torch
+    g = golden("p3_worked_example.txt")
+    cu_pad = [int(v) for v in g["cu_seqlens_padded"]]
+    cu = [int(v) for v in g["cu_seqlens"]]
+    route = thd.Route(3, 2, 16)
+    route.build(dev_i32(cu_pad), 2, 16)
+    _, mask, status = route.roll_labels_zigzag(dev_i64(np.arange(16)), dev_i32(cu_pad), dev_i32(cu), 1, 0)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    m = mask[0].cpu().numpy().tolist()
+    assert m[:8] == [int(v) for v in g["rank0_valid_mask"]]
+    assert m[8:] == [int(v) for v in g["rank1_valid_mask"]]
+
+
+def test_roll_zigzag_bad_route_writes_nothing(thd):
+    import torch
+    route = thd.Route(2, 2, 16)
+    route.build(dev_i32([0, 6, 16]), 2, 16)           # length 6 not a multiple of 4
+    shifted = torch.full((1, 16), -3, dtype=torch.int64, device="cuda")
+    mask = torch.full((2, 16), 9, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    code = thd.thd_roll_labels_zigzag(route.handle, torch.arange(16, device="cuda"), dev_i32([0, 6, 16]), None, 2,
+                                      16, 1, 0, shifted, mask, status)
+    assert code == thd.THD_OK
+    torch.cuda.synchronize()
+    assert int(status.item()) == thd.THD_ERR_CU_DIVISIBLE
+    assert (shifted == -3).all() and (mask == 9).all()
+    with pytest.raises(thd.ThdError) as e:
+        thd.thd_roll_labels_zigzag(route.handle, torch.arange(8, device="cuda"), dev_i32([0, 8]), None, 1, 8, 1, 0,
+                                   shifted, mask, status)
+    assert e.value.code == thd.THD_ERR_SHAPE
+
+
+def test_graph_capture_replays_build_swaps_and_roll(thd):
+    # Capture one micro-batch (build, 8 layers x 2 swaps, zigzag roll) in a
+    # HIP graph; replay it several times with eager work in between, and once
+    # after writing different boundaries into the captured buffer.
+    import torch
+    wa = W.random_packed(500, 4, 30, 40, 2, pad_max=3, row_shape=(2048,), row_dtype="uint8")
+    total, cp = wa.total, wa.cp
+    # a second batch with the same token and slot counts: the documents reordered
+    perm = np.random.default_rng(7).permutation(wa.n_slots)
+    wb = W.Workload("reordered", 100, cp, W.cumulative(np.diff(wa.cu_padded)[perm]),
+                    W.cumulative(np.diff(wa.cu_real)[perm]), (2048,), row_dtype="uint8", max_shift=1,
+                    seed_extra=(501,))
+    assert not np.array_equal(wb.cu_padded, wa.cu_padded)
+    route = thd.Route(wa.n_slots, cp, total)
+    cu = dev_i32(wa.cu_padded)
+    cu_real = dev_i32(wa.cu_real)
+    x = torch.from_numpy(wa.rows_host()).cuda()
+    ids = dev_i64(wa.ids())
+    a, b = torch.empty_like(x), torch.empty_like(x)
+    shifted = torch.empty((2, total), dtype=torch.int64, device="cuda")
+    mask = torch.empty((3, total), dtype=torch.uint8, device="cuda")
+    status = torch.empty(1, dtype=torch.int32, device="cuda")
+    n_slots = wa.n_slots
+
+    def step(stream):
+        thd.thd_build_route(route.handle, cu, n_slots, cp, total, stream)
+        for _ in range(8):
+            thd.thd_swap(route.handle, thd.Z2C, x, a, total, 2048, stream)
+            thd.thd_swap(route.handle, thd.C2Z, a, b, total, 2048, stream)
+        thd.thd_roll_labels_zigzag(route.handle, ids, cu, cu_real, n_slots, total, 2, 0, shifted, mask, status,
+                                   stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s.cuda_stream)                          # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+    def expect(w):
+        want_a = O.swap_rows(w.rows_host(), w.cu_padded, cp, total, "z2c")
+        ws, wm = O.roll_labels(w.ids(), w.cu_padded, w.cu_real, total, 2, 0)
+        return want_a, [O.swap_rows(ws[k], w.cu_padded, cp, total, "c2z") for k in range(2)], \
+            [O.swap_rows(wm[k], w.cu_padded, cp, total, "c2z") for k in range(3)]
+
+    want_a, want_s, want_m = expect(wa)
+    for rep in range(3):
+        a.zero_(); b.zero_(); shifted.zero_(); mask.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        assert int(status.item()) == 0
+        assert np.array_equal(a.cpu().numpy(), want_a)
+        assert torch.equal(b, x)
+        for k in range(2):
+            assert np.array_equal(shifted[k].cpu().numpy(), want_s[k])
+        for k in range(3):
+            assert np.array_equal(mask[k].cpu().numpy(), want_m[k])
+        _ = (x.float().sum() + 1).item()             # eager work between replays
+    cu.copy_(dev_i32(wb.cu_padded))
+    cu_real.copy_(dev_i32(wb.cu_real))
+    x.copy_(torch.from_numpy(wb.rows_host()).cuda())
+    ids.copy_(dev_i64(wb.ids()))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    want_a, want_s, want_m = expect(wb)
+    assert np.array_equal(a.cpu().numpy(), want_a)
+    for k in range(2):
+        assert np.array_equal(shifted[k].cpu().numpy(), want_s[k])

@@ -118,6 +118,7 @@ def test_random_swap_parity(thd, case):
     (20000, 0, 1, 512, 1, 4096), (20000, 5, 0, 1024, 2, 4096), (1000, 0, 1, 128, 2, 4096),
     (3 * 4096, 13, 1, 256, 1, 4096), (0, 0, 1, 0, 0, 8192), (0, 9, 1, 0, 0, 8192), (0, 0, 0, 0, 0, 8208),
     (0, 0, 1, 0, 0, 4096), (0, 6, 1, 0, 0, 4096), (0, 0, 1, 0, 2, 2048), (5000, 0, 1, 0, 2, 36),
+    (0, 7, 1, 0, 0, 8), (0, 3, 1, 0, 0, 1), (0, 0, 0, 0, 0, 16), (0, 5, 1, 0, 0, 2),
 ])
 def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt, block, order, rb):
     import torch
@@ -223,6 +224,23 @@ def test_route_build_slow_paths(thd, seed, cp, docs, max_chunk, n_empty):
     say("slow path", seed, cp, "slots", w.n_slots, "T", total)
     route = build(thd, cu, cp, total)
     check_route_matches_oracle(route, cu, cp, total)
+    x = torch.from_numpy(w.rows_host()).cuda()
+    for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+        out = route.swap(x, d)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), O.swap_rows(w.rows_host(), cu, cp, total, direction)), direction
+
+
+@pytest.mark.parametrize("seed,cp,rb", [(300, 2, 8), (301, 3, 1), (302, 3, 8), (303, 5, 4), (304, 2, 16)])
+def test_small_rows_with_dense_runs(thd, seed, cp, rb):
+    # One-unit rows through the LDS-staged small-row path, on batches of
+    # 2*cp-token documents whose runs are so short that some tiles overflow
+    # the staged run window and take the piecewise fallback.
+    import torch
+    w = W.random_packed(seed, cp, 4000, 1, 50, row_shape=(rb,), row_dtype="uint8")
+    cu, total = w.cu_padded, w.total
+    say("small rows", seed, cp, rb, "T", total)
+    route = build(thd, cu, cp, total)
     x = torch.from_numpy(w.rows_host()).cuda()
     for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
         out = route.swap(x, d)
