@@ -169,7 +169,7 @@ __global__ __launch_bounds__(BLOCK) void swap_small_kernel(const int32_t* __rest
   const int32_t n_runs = hdr[runs_word];
   constexpr int32_t kTileRows = BLOCK * kSmallRowsPerThread;
   for (int32_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int32_t r0 = tile * kTileRows;
+    const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(tile) * kTileRows);
     const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + kTileRows));
     swap_tile_small<U, BLOCK, NT>(runs, dir, n_runs, in, out, total, r0, r1, s_runs, s_k);
   }

@@ -37,6 +37,7 @@ from .thd_oracle import (  # noqa: F401
     check_roll_boundaries,
     contiguous_rank_tokens,
     zigzag_rank_tokens,
+    zigzag_position,
     layout_tokens,
     build_route,
     canonical_runs,

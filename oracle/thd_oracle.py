@@ -105,6 +105,30 @@ def zigzag_rank_tokens(cu, cp: int, rank: int) -> np.ndarray:
     return np.asarray(tokens, dtype=np.int64)
 
 
+def zigzag_position(cu, cp: int, total: int, token: int) -> int:
+    """Emulated zigzag row of one token, for checking huge batches one token
+    at a time.
+
+    The same definition as ``zigzag_rank_tokens`` ("Packed Sequence 与上下文并行"
+    §2.4), read for a single token: in its slot the token sits in chunk q;
+    the rank owning q is the r with q in {r, 2*cp-1-r}; on that rank every
+    earlier slot contributed two chunks, and within the slot chunk r comes
+    before chunk 2*cp-1-r.
+    """
+    b = _as_int_list(cu)
+    before = 0                                    # rows each rank holds from earlier slots
+    for s in range(len(b) - 1):
+        start, end = b[s], b[s + 1]
+        chunk = (end - start) // (2 * cp)
+        if start <= token < end:
+            q = (token - start) // chunk
+            rank = q if q < cp else 2 * cp - 1 - q
+            local = before + (0 if q == rank else chunk) + (token - start - q * chunk)
+            return rank * (total // cp) + local
+        before += 2 * chunk
+    raise OracleInputError("ARG", f"token {token} outside the batch")
+
+
 def contiguous_rank_tokens(total: int, cp: int, rank: int) -> np.ndarray:
     """Global token ids owned by ``rank`` under the contiguous (Ulysses) slice.
 

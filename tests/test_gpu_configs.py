@@ -126,3 +126,46 @@ def test_workload_roll(thd, name):
     assert int(status.item()) == 0
     assert np.array_equal(shifted.cpu().numpy(), want_s)
     assert np.array_equal(mask.cpu().numpy(), want_m)
+
+
+def test_maximum_size_swap(thd):
+    # T = 2**31 - 64 tokens (int32 boundaries at their limit), 1-byte rows:
+    # 2 GiB per buffer.  The route is checked run by run and token by token
+    # with the oracle's single-token form; the swap on sampled rows and by the
+    # round trip.
+    import torch
+    cp = 2
+    total = 2 ** 31 - 64
+    lens = [1 << 29, 123456788, 4, 1000000000, 0]
+    lens[-1] = total - sum(lens[:-1])
+    assert all(v % (2 * cp) == 0 for v in lens) and sum(lens) == total
+    cu = W.cumulative(lens)
+    say("maximum size", total)
+    route = thd.Route(len(lens), cp, total)
+    route.build(dev_i32(cu), cp, total)
+    assert route.status() == 0
+    by_src, by_dst, split = route.copy_out()
+    share = total // cp
+    assert (split.astype(np.int64).sum(0) == share).all() and (split.astype(np.int64).sum(1) == share).all()
+    for order, col in ((by_src, 0), (by_dst, 1)):
+        starts = order[:, col].astype(np.int64)
+        assert starts[0] == 0 and np.array_equal(starts[1:], starts[:-1] + order[:-1, 2])
+        assert int(order[:, 2].astype(np.int64).sum()) == total
+    for zrow, tok, n in by_src.astype(np.int64):
+        for off in (0, n - 1):
+            assert O.zigzag_position(cu, cp, total, int(tok + off)) == zrow + off
+    x = torch.randint(0, 256, (total, 1), dtype=torch.uint8, device="cuda")
+    out = route.swap(x, thd.Z2C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    toks = np.unique(np.concatenate([rng.integers(0, total, 3000), by_src[:, 1].astype(np.int64),
+                                     by_src[:, 1].astype(np.int64) + by_src[:, 2] - 1, [0, total - 1]]))
+    src = np.array([O.zigzag_position(cu, cp, total, int(t)) for t in toks], dtype=np.int64)
+    got = out.view(-1).index_select(0, torch.from_numpy(toks).cuda()).cpu().numpy()
+    want = x.view(-1).index_select(0, torch.from_numpy(src).cuda()).cpu().numpy()
+    assert np.array_equal(got, want)
+    back = route.swap(out, thd.C2Z)
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    del x, out, back, route
+    torch.cuda.empty_cache()

@@ -112,6 +112,19 @@ def test_zigzag_matches_sort_key_and_closed_form(cp):
     assert n > 10
 
 
+@pytest.mark.parametrize("cp", [1, 2, 3, 4])
+def test_single_token_form_matches_the_lists(cp):
+    # zigzag_position (used to check huge batches token by token) against the
+    # per-rank lists, on every small case.
+    for cpc, cu in CASES:
+        if cpc != cp:
+            continue
+        total = cu[-1]
+        z = O.layout_tokens(cu, cp, total, O.ZIGZAG)
+        for row, g in enumerate(z.tolist()):
+            assert O.zigzag_position(cu, cp, total, g) == row, (cu, g)
+
+
 @pytest.mark.parametrize("cp", [2, 3, 4])
 def test_route_invariants(cp):
     rng = np.random.default_rng(7)
