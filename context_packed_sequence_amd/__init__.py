@@ -27,6 +27,8 @@ from .binding import (  # noqa: F401
     THD_ERR_HIP,
     THD_ERR_INTEGRITY,
     THD_ERR_NOT_BUILT,
+    THD_ERR_PACK_CAPACITY,
+    THD_ERR_PACK_DOCS,
     THD_ERR_REAL_GT_PADDED,
     THD_ERR_SHAPE,
     THD_IDENTITY,
@@ -37,6 +39,8 @@ from .binding import (  # noqa: F401
     THD_ZIGZAG_TO_CONTIGUOUS,
     ThdError,
     thd_build_route,
+    thd_pack,
+    thd_pack_workspace_bytes,
     thd_roll_labels,
     thd_roll_labels_zigzag,
     thd_route_copy_out,
@@ -151,3 +155,23 @@ def roll_labels(ids, cu_seqlens_padded, cu_seqlens=None, max_shift: int = 1, fil
     thd_roll_labels(ids, cu_seqlens_padded, cu_seqlens, n_slots, total, max_shift, fill, shifted, mask, status,
                     stream)
     return shifted, mask, status
+
+
+def pack(tokens, pad_id: int, eod_id: int, align: int, capacity: int, max_docs: int, pad_value: int = 0,
+         stream=None):
+    """Pack [batch, seq] int64 token rows on the device.  Returns (packed
+    [capacity] int64, cu_seqlens [max_docs + 2] int32, cu_seqlens_padded
+    [max_docs + 2] int32, status int32 [1]); the route and the roll take
+    n_slots = max_docs + 1 and total_tokens = capacity."""
+    import torch
+    batch, seq = (int(tokens.shape[0]), int(tokens.shape[1])) if tokens.dim() == 2 else (1, int(tokens.numel()))
+    dev = tokens.device
+    nbytes = thd_pack_workspace_bytes(batch, seq)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    packed = torch.empty(capacity, dtype=torch.int64, device=dev)
+    cu_real = torch.empty(max_docs + 2, dtype=torch.int32, device=dev)
+    cu_pad = torch.empty(max_docs + 2, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    thd_pack(tokens, batch, seq, pad_id, eod_id, align, capacity, max_docs, pad_value, workspace, nbytes, packed,
+             cu_real, cu_pad, status, stream)
+    return packed, cu_real, cu_pad, status

@@ -37,6 +37,8 @@ THD_ERR_CU_TOTAL = -12
 THD_ERR_CU_DIVISIBLE = -13
 THD_ERR_REAL_GT_PADDED = -14
 THD_ERR_INTEGRITY = -15
+THD_ERR_PACK_DOCS = -16
+THD_ERR_PACK_CAPACITY = -17
 
 THD_ZIGZAG_TO_CONTIGUOUS = 0
 THD_CONTIGUOUS_TO_ZIGZAG = 1
@@ -47,7 +49,7 @@ THD_MAX_BATCH = 16
 EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",
     "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_swap_tuning", "thd_strerror",
-    "thd_swap_batch", "thd_roll_labels_zigzag",
+    "thd_swap_batch", "thd_roll_labels_zigzag", "thd_pack_workspace_bytes", "thd_pack",
 )
 
 
@@ -80,6 +82,9 @@ def _load() -> ctypes.CDLL:
                                           ctypes.POINTER(c_i64), c_i64, c_p]),
         "thd_roll_labels_zigzag": (ctypes.c_int, [c_p, c_p, c_p, c_p, c_i32, c_i64, c_i32, c_i64, c_p, c_p, c_p,
                                                   c_p]),
+        "thd_pack_workspace_bytes": (ctypes.c_int64, [c_i32, c_i32]),
+        "thd_pack": (ctypes.c_int, [c_p, c_i32, c_i32, c_i64, c_i64, c_i32, c_i64, c_i32, c_i64, c_p, c_i64, c_p,
+                                    c_p, c_p, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -171,6 +176,18 @@ def thd_roll_labels_zigzag(route: int, ids, cu_seqlens_padded, cu_seqlens, n_slo
     return _check(_lib.thd_roll_labels_zigzag(route, _ptr(ids), _ptr(cu_seqlens_padded), _ptr(cu_seqlens),
                                               n_slots, total_tokens, max_shift, fill, _ptr(shifted), _ptr(mask),
                                               _ptr(status), _stream(stream)), "thd_roll_labels_zigzag")
+
+
+def thd_pack_workspace_bytes(batch: int, seq: int) -> int:
+    return int(_lib.thd_pack_workspace_bytes(batch, seq))
+
+
+def thd_pack(tokens, batch: int, seq: int, pad_id: int, eod_id: int, align: int, capacity: int, max_docs: int,
+             pad_value: int, workspace, workspace_bytes: int, packed, cu_seqlens, cu_seqlens_padded, status,
+             stream=None) -> int:
+    return _check(_lib.thd_pack(_ptr(tokens), batch, seq, pad_id, eod_id, align, capacity, max_docs, pad_value,
+                                _ptr(workspace), workspace_bytes, _ptr(packed), _ptr(cu_seqlens),
+                                _ptr(cu_seqlens_padded), _ptr(status), _stream(stream)), "thd_pack")
 
 
 def thd_route_status(route: int, stream=None) -> int:

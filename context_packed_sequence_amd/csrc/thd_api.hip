@@ -86,6 +86,8 @@ const char* thd_strerror(int32_t code) {
     case THD_ERR_CU_DIVISIBLE: return "a sequence length is not a multiple of 2*cp_size";
     case THD_ERR_REAL_GT_PADDED: return "a real sequence length exceeds its padded length";
     case THD_ERR_INTEGRITY: return "route integrity check failed";
+    case THD_ERR_PACK_DOCS: return "more documents than document slots";
+    case THD_ERR_PACK_CAPACITY: return "padded documents exceed the token budget";
     default: return "unknown code";
   }
 }
@@ -247,6 +249,71 @@ int thd_swap_batch(const thd_route* route, int32_t direction, int32_t n_tensors,
   const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
   if (thdcp::launch_swap_batch(route->dev.hdr, runs, word, dir, n_tensors, ins, outs, row_bytes,
                                static_cast<int32_t>(rows), as_stream(stream)) != hipSuccess)
+    return THD_ERR_HIP;
+  return THD_OK;
+}
+
+namespace {
+
+struct PackLayout {
+  int64_t hdr, ends, row_valid, row_docs, row_padded, row_doc_off, row_real_off, row_pack_off, bytes;
+};
+
+PackLayout pack_layout(int64_t batch, int64_t seq) {
+  PackLayout l{};
+  int64_t off = 0;
+  l.hdr = off;          off = align_up(off + 64, 256);
+  l.ends = off;         off = align_up(off + batch * seq * 4, 256);
+  l.row_valid = off;    off = align_up(off + batch * 4, 256);
+  l.row_docs = off;     off = align_up(off + batch * 4, 256);
+  l.row_padded = off;   off = align_up(off + batch * 8, 256);
+  l.row_doc_off = off;  off = align_up(off + batch * 8, 256);
+  l.row_real_off = off; off = align_up(off + batch * 8, 256);
+  l.row_pack_off = off; off = align_up(off + batch * 8, 256);
+  l.bytes = off;
+  return l;
+}
+
+}  // namespace
+
+int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq) {
+  if (batch < 0 || seq < 0) return -1;
+  return pack_layout(batch, seq).bytes;
+}
+
+int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id, int32_t align,
+             int64_t capacity, int32_t max_docs, int64_t pad_value, void* workspace, int64_t workspace_bytes,
+             int64_t* packed, int32_t* cu_seqlens, int32_t* cu_seqlens_padded, int32_t* status, void* stream) {
+  if (batch < 0 || seq < 0 || align < 1 || capacity < 0 || capacity > INT32_MAX || capacity % align != 0 ||
+      max_docs < 0 || max_docs > INT32_MAX - 2 || pad_id == eod_id)
+    return THD_ERR_ARG;
+  const int64_t n_tok = static_cast<int64_t>(batch) * seq;
+  const PackLayout l = pack_layout(batch, seq);
+  if (!workspace || workspace_bytes < l.bytes || !cu_seqlens || !cu_seqlens_padded) return THD_ERR_ARG;
+  if ((n_tok > 0 && !tokens) || (capacity > 0 && !packed)) return THD_ERR_ARG;
+  const int64_t cu_bytes = (static_cast<int64_t>(max_docs) + 2) * 4;
+  const struct {
+    const void* p;
+    int64_t n;
+  } outs[] = {{packed, capacity * 8}, {cu_seqlens, cu_bytes}, {cu_seqlens_padded, cu_bytes}, {status, status ? 4 : 0},
+              {workspace, l.bytes}};
+  for (size_t i = 0; i < 5; ++i) {
+    if (overlaps(outs[i].p, outs[i].n, tokens, n_tok * 8)) return THD_ERR_ALIAS;
+    for (size_t j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return THD_ERR_ALIAS;
+  }
+  char* w = static_cast<char*>(workspace);
+  thdcp::PackWs ws;
+  ws.hdr = reinterpret_cast<int32_t*>(w + l.hdr);
+  ws.ends = reinterpret_cast<int32_t*>(w + l.ends);
+  ws.row_valid = reinterpret_cast<int32_t*>(w + l.row_valid);
+  ws.row_docs = reinterpret_cast<int32_t*>(w + l.row_docs);
+  ws.row_padded = reinterpret_cast<int64_t*>(w + l.row_padded);
+  ws.row_doc_off = reinterpret_cast<int64_t*>(w + l.row_doc_off);
+  ws.row_real_off = reinterpret_cast<int64_t*>(w + l.row_real_off);
+  ws.row_pack_off = reinterpret_cast<int64_t*>(w + l.row_pack_off);
+  if (thdcp::launch_pack(tokens, batch, seq, pad_id, eod_id, align, static_cast<int32_t>(capacity), max_docs,
+                         pad_value, ws, packed, cu_seqlens, cu_seqlens_padded, status, as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;
   return THD_OK;
 }

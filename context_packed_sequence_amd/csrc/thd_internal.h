@@ -88,6 +88,22 @@ hipError_t launch_roll(const int64_t* ids, const int32_t* cu_pad, const int32_t*
                        int64_t* shifted, uint8_t* mask, int32_t* status, const RollRoute* route,
                        hipStream_t stream);
 
+// Views into the caller's packing workspace (see thd_pack_workspace_bytes).
+struct PackWs {
+  int32_t* hdr;          // [0] status, [1] documents, [2] padded tokens
+  int32_t* ends;         // [batch][seq] document ends per row (exclusive, row coordinates)
+  int32_t* row_valid;    // [batch] valid end of each row (= its real tokens)
+  int32_t* row_docs;     // [batch]
+  int64_t* row_padded;   // [batch] padded tokens of the row's documents
+  int64_t* row_doc_off;  // [batch] exclusive prefix sums over rows
+  int64_t* row_real_off;
+  int64_t* row_pack_off;
+};
+
+hipError_t launch_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id,
+                       int32_t align, int32_t capacity, int32_t max_docs, int64_t pad_value, const PackWs& ws,
+                       int64_t* packed, int32_t* cu_real, int32_t* cu_pad, int32_t* status, hipStream_t stream);
+
 // Severity of a validation failure: larger wins; 0 = no failure.
 __host__ __device__ inline int32_t severity_to_code(int sev) {
   switch (sev) {

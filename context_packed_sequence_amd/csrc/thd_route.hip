@@ -23,6 +23,7 @@
 // for the back chunk).  Cutting it at multiples of T/cp (the contiguous ranks'
 // borders) gives the route's pieces; pieces that touch in both coordinates
 // inside one (source rank, destination rank) pair are merged into one run.
+#include "thd_device.h"
 #include "thd_internal.h"
 
 namespace thdcp {
@@ -30,37 +31,6 @@ namespace {
 
 constexpr int kBuildThreads = 1024;
 constexpr int kBuildWaves = kBuildThreads / 64;
-
-// Exclusive prefix sum over the workgroup.  Every thread must call it; it
-// returns the thread's exclusive offset and the workgroup total in *total.
-__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    const int w = lane < kBuildWaves ? s_wave[lane] : 0;
-    int xs = w;
-#pragma unroll
-    for (int o = 1; o < kBuildWaves; o <<= 1) {
-      const int y = __shfl_up(xs, o, 64);
-      if (lane >= o) xs += y;
-    }
-    if (lane < kBuildWaves) s_wave[lane] = xs - w;
-    if (lane == kBuildWaves - 1) s_wave[kBuildWaves] = xs;
-  }
-  __syncthreads();
-  const int excl = s_wave[wave] + x - v;
-  *total = s_wave[kBuildWaves];
-  __syncthreads();
-  return excl;
-}
 
 struct Segment {
   int32_t tok;   // first global token
@@ -147,7 +117,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
       else len = static_cast<int32_t>(d);
     }
     int sum;
-    const int off = block_exclusive_scan(len > 0 ? 1 : 0, s_wave, &sum);
+    const int off = block_exclusive_scan<kBuildThreads, int>(len > 0 ? 1 : 0, s_wave, &sum);
     if (len > 0) {
       const int32_t k = n_docs + off;
       docs[k] = a;
@@ -217,7 +187,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     const int count_s = j < n_seg ? cs.pieces - merge_s : 0;
     const int count_t = j < n_seg ? ct.pieces - merge_t : 0;
     int sum;
-    const int off = block_exclusive_scan(count_s | (count_t << 16), s_wave, &sum);
+    const int off = block_exclusive_scan<kBuildThreads, int>(count_s | (count_t << 16), s_wave, &sum);
     if (j < n_seg) {
       const int32_t off_s = off & 0xFFFF, off_t = off >> 16;
       for (int p = 0; p < cs.pieces; ++p) {

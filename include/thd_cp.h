@@ -63,6 +63,8 @@ extern "C" {
 #define THD_ERR_CU_DIVISIBLE  -13   /* a slot length is not a multiple of 2*cp_size    */
 #define THD_ERR_REAL_GT_PADDED -14  /* roll: real length above padded length           */
 #define THD_ERR_INTEGRITY     -15   /* route self-check failed (internal error)        */
+#define THD_ERR_PACK_DOCS     -16   /* pack: more documents than max_docs              */
+#define THD_ERR_PACK_CAPACITY -17   /* pack: padded documents longer than capacity     */
 
 /* ---- directions ---------------------------------------------------------- */
 #define THD_ZIGZAG_TO_CONTIGUOUS 0
@@ -201,6 +203,48 @@ int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const 
 int thd_roll_labels_zigzag(const thd_route* route, const int64_t* ids, const int32_t* cu_seqlens_padded,
                            const int32_t* cu_seqlens, int32_t n_slots, int64_t total_tokens, int32_t max_shift,
                            int64_t fill, int64_t* shifted, uint8_t* mask, int32_t* status, void* stream);
+
+/*
+ * thd_pack_workspace_bytes -- device workspace thd_pack needs for a
+ * [batch, seq] token matrix (host-only arithmetic; -1 for negative sizes).
+ */
+int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq);
+
+/*
+ * thd_pack -- pack [batch, seq] token rows into one padded THD stream on the
+ * device ("Packed Sequence 与上下文并行" §2.2 steps (1)-(3), worked example
+ * §3.1-§3.4), with every output shape fixed by the arguments so that the route
+ * build, the swaps and the roll can follow without the host reading anything.
+ *
+ * tokens:    device int64 [batch][seq], row-major.
+ * Documents: in each row the valid part ends after the last token that is not
+ *            pad_id; inside it every eod_id token closes a document (the EOD is
+ *            its last token) and the tokens after the last EOD form one more
+ *            document.  pad_id tokens before the valid end stay in their
+ *            document.  Rows in order, documents left to right.
+ * align:     each document is padded at its end to a multiple of align (the
+ *            pages use TP*CP*2, or TP*CP*16 with FP8; a multiple of 2*cp_size
+ *            is what the route needs).
+ * capacity:  token budget of the packed stream, a multiple of align, at most
+ *            INT32_MAX.  packed: device int64 [capacity]; positions holding no
+ *            token get pad_value.
+ * max_docs:  document slots.  cu_seqlens / cu_seqlens_padded: device int32
+ *            [max_docs + 2] (real / padded boundaries, n_slots = max_docs + 1):
+ *            slot k < n_docs is document k, slot n_docs is the trailing
+ *            pad-only slot up to capacity (real length 0), later slots are
+ *            empty (a repeated boundary).
+ * workspace: device buffer of at least thd_pack_workspace_bytes(batch, seq).
+ * status:    device int32 or NULL: THD_OK, THD_ERR_PACK_DOCS or
+ *            THD_ERR_PACK_CAPACITY; on an error nothing but status is written.
+ *
+ * Host errors: THD_ERR_ARG (negative sizes, align < 1, capacity not a multiple
+ * of align, pad_id == eod_id, null pointers, workspace too small),
+ * THD_ERR_ALIAS (outputs overlapping each other, the tokens or the workspace).
+ * Three kernel launches.
+ */
+int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id, int32_t align,
+             int64_t capacity, int32_t max_docs, int64_t pad_value, void* workspace, int64_t workspace_bytes,
+             int64_t* packed, int32_t* cu_seqlens, int32_t* cu_seqlens_padded, int32_t* status, void* stream);
 
 /*
  * thd_route_status -- SYNC.  Waits for `stream`, then stores the status word

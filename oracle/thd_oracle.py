@@ -355,3 +355,67 @@ def roll_labels(ids, cu_padded, cu_real, total: int, max_shift: int, fill: int =
                 shifted[j - 1, begin:last] = ids[begin + j:end_real]
                 mask[j, begin:last] = 1
     return shifted, mask
+
+
+# ---------------------------------------------------------------------------
+# Packing ("Packed Sequence 与上下文并行" §2.2 steps (1)-(3), §3.2-§3.4).
+# ---------------------------------------------------------------------------
+
+def pack_batch(tokens, pad_id: int, eod_id: int, align: int, capacity: int, max_docs: int, pad_value: int):
+    """Pack a [batch, seq] token matrix into one padded THD stream.
+
+    Steps of §2.2, in order:
+
+    1. documents: in each row the valid part ends after the last non-PAD
+       token; inside it every EOD token closes a document (the EOD belongs to
+       the document it closes) and whatever follows the last EOD is one more
+       document.  PAD tokens before the end of the valid part stay inside
+       their document.  Rows are taken in order, documents left to right.
+    2. alignment: each document is padded at its end to a multiple of
+       ``align`` (the page's TP*CP*2, or TP*CP*16 with FP8);
+    3. flattening: documents are laid end to end at their padded offsets and
+       every position that holds no token gets ``pad_value``.
+
+    A fixed token budget keeps the output shape independent of the data: the
+    stream is ``capacity`` long, the space after the last document is one
+    trailing pad-only slot, and the document slots not used are empty (a
+    repeated boundary).  Returns ``(packed int64 [capacity], cu_seqlens int32
+    [max_docs + 2], cu_seqlens_padded int32 [max_docs + 2])``: slot k < n_docs
+    is document k, slot n_docs the trailing pad slot, later slots are empty.
+    Raises PACK_DOCS when there are more than ``max_docs`` documents and
+    PACK_CAPACITY when the padded documents do not fit in ``capacity``.
+    """
+    if align < 1 or capacity < 0 or max_docs < 0 or capacity % align != 0 or pad_id == eod_id:
+        raise OracleInputError("ARG", "bad pack arguments")
+    rows = np.asarray(tokens, dtype=np.int64)
+    rows = rows.reshape(-1, rows.shape[-1]) if rows.size else rows.reshape(-1, max(rows.shape[-1:] or [0]))
+    docs = []                                           # (row, start, end) in row coordinates
+    for b in range(rows.shape[0]):
+        row = rows[b]
+        non_pad = [s for s in range(row.shape[0]) if row[s] != pad_id]
+        valid_end = non_pad[-1] + 1 if non_pad else 0
+        start = 0
+        for s in range(valid_end):
+            if row[s] == eod_id:
+                docs.append((b, start, s + 1))
+                start = s + 1
+        if start < valid_end:
+            docs.append((b, start, valid_end))
+    lengths = [e - s for _, s, e in docs]
+    padded = [n + (-n) % align for n in lengths]
+    if len(docs) > max_docs:
+        raise OracleInputError("PACK_DOCS", f"{len(docs)} documents, room for {max_docs}")
+    if sum(padded) > capacity:
+        raise OracleInputError("PACK_CAPACITY", f"{sum(padded)} padded tokens, room for {capacity}")
+    cu_real = np.zeros(max_docs + 2, dtype=np.int64)
+    cu_pad = np.zeros(max_docs + 2, dtype=np.int64)
+    for k, (n, p) in enumerate(zip(lengths, padded)):
+        cu_real[k + 1] = cu_real[k] + n
+        cu_pad[k + 1] = cu_pad[k] + p
+    n_docs = len(docs)
+    cu_real[n_docs + 1:] = cu_real[n_docs]              # trailing pad slot and empty slots: no real tokens
+    cu_pad[n_docs + 1:] = capacity                      # trailing pad slot ends at the budget; the rest are empty
+    packed = np.full(capacity, pad_value, dtype=np.int64)
+    for k, (b, s, e) in enumerate(docs):
+        packed[cu_pad[k]:cu_pad[k] + (e - s)] = rows[b, s:e]
+    return packed, cu_real.astype(np.int32), cu_pad.astype(np.int32)

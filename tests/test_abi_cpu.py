@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "thd_cp.h")
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    names = re.findall(r"\b(?:int|void|const char\s*\*)\s+(thd_[a-z_]+)\s*\(", text)
+    names = re.findall(r"\b(?:int64_t|int|void|const char\s*\*)\s+(thd_[a-z_]+)\s*\(", text)
     return sorted(set(names))
 
 
@@ -81,6 +81,24 @@ def test_host_rejections_without_device_work(pkg):
     assert lib.thd_roll_labels(8, None, None, 1, 8, 1, 0, 4096, 8192, None, None) == pkg.THD_ERR_ARG
     assert lib.thd_roll_labels(4096, 16, None, 1, 8, 1, 0, 4096 + 8, 1 << 20, None, None) == pkg.THD_ERR_ALIAS
     assert lib.thd_roll_labels(1 << 20, 16, None, 1, 8, 2, 0, 4096, 4096 + 64, None, None) == pkg.THD_ERR_ALIAS
+    # pack: bad sizes, alignment, ids, workspace, overlapping outputs
+    ws = lib.thd_pack_workspace_bytes(2, 8)
+    assert ws > 0 and lib.thd_pack_workspace_bytes(-1, 8) == -1
+    good = dict(tokens=1 << 20, batch=2, seq=8, pad=0, eod=1, align=4, cap=16, max_docs=4, fill=0,
+                ws=1 << 24, ws_bytes=ws, packed=1 << 28, cu=1 << 30, cup=1 << 31, status=None)
+
+    def pack(**kw):
+        a = dict(good, **kw)
+        return lib.thd_pack(a["tokens"], a["batch"], a["seq"], a["pad"], a["eod"], a["align"], a["cap"],
+                            a["max_docs"], a["fill"], a["ws"], a["ws_bytes"], a["packed"], a["cu"], a["cup"],
+                            a["status"], None)
+    assert pack(align=0) == pkg.THD_ERR_ARG
+    assert pack(cap=18) == pkg.THD_ERR_ARG
+    assert pack(eod=0) == pkg.THD_ERR_ARG
+    assert pack(ws_bytes=ws - 1) == pkg.THD_ERR_ARG
+    assert pack(batch=-1) == pkg.THD_ERR_ARG
+    assert pack(cu=(1 << 31) + 8) == pkg.THD_ERR_ALIAS
+    assert pack(packed=(1 << 20) + 64) == pkg.THD_ERR_ALIAS
     # tuning argument checks
     assert lib.thd_swap_tuning(-1, 0, 1, 0, 0) == pkg.THD_ERR_ARG
     assert lib.thd_swap_tuning(0, -1, 1, 0, 0) == pkg.THD_ERR_ARG

@@ -95,7 +95,42 @@ def _check_monotone_skipped(cu, cp, total):
     return b
 
 
+_real_pack = T.pack_batch
+
+
+def _pack_eod_starts_next(tokens, pad_id, eod_id, align, capacity, max_docs, pad_value):
+    # EOD opens the next document instead of closing its own
+    rows = np.asarray(tokens, dtype=np.int64)
+    shifted = rows.copy()
+    for b in range(rows.shape[0]):
+        for s in range(rows.shape[1] - 1, 0, -1):
+            if rows[b, s - 1] == eod_id and rows[b, s] != pad_id:
+                shifted[b, s - 1], shifted[b, s] = rows[b, s], rows[b, s - 1]
+    return _real_pack(shifted, pad_id, eod_id, align, capacity, max_docs, pad_value)
+
+
+def _pack_drops_trailing(tokens, pad_id, eod_id, align, capacity, max_docs, pad_value):
+    rows = np.asarray(tokens, dtype=np.int64).copy()
+    for b in range(rows.shape[0]):
+        eods = np.flatnonzero(rows[b] == eod_id)
+        cut = eods[-1] + 1 if eods.size else 0
+        rows[b, cut:] = pad_id
+    return _real_pack(rows, pad_id, eod_id, align, capacity, max_docs, pad_value)
+
+
+def _pack_valid_end_at_first_pad(tokens, pad_id, eod_id, align, capacity, max_docs, pad_value):
+    rows = np.asarray(tokens, dtype=np.int64).copy()
+    for b in range(rows.shape[0]):
+        pads = np.flatnonzero(rows[b] == pad_id)
+        if pads.size:
+            rows[b, pads[0]:] = pad_id
+    return _real_pack(rows, pad_id, eod_id, align, capacity, max_docs, pad_value)
+
+
 MUTATIONS = {
+    "pack: EOD opens the next document": ("pack_batch", _pack_eod_starts_next),
+    "pack: document after the last EOD dropped": ("pack_batch", _pack_drops_trailing),
+    "pack: valid part ends at the first PAD": ("pack_batch", _pack_valid_end_at_first_pad),
     "back chunk index off by one": ("zigzag_rank_tokens", _zig_back_off_by_one),
     "back chunk before front chunk": ("zigzag_rank_tokens", _zig_back_first),
     "chunks of L/cp": ("zigzag_rank_tokens", _zig_chunk_by_cp),
@@ -137,6 +172,10 @@ def run_pins():
         ("a2a", lambda: BF.test_emulated_all_to_all_matches_global_swap(2)),
         ("np.roll", BF.test_roll_matches_per_document_numpy_roll),
         ("no crossing", lambda: BF.test_roll_counts_and_no_crossing(1)),
+        ("pack example", lambda: P.test_pack_reproduces_the_worked_example(worked)),
+        ("pack budget", P.test_pack_budget_and_empty_slots),
+        ("pack corners", lambda: [P.test_pack_corner_cases(r, d) for r, d in (
+            (["a_bE__"], ["a_bE"]), (["aEbc_"], ["aE", "bc"]), (["EE_", "a__"], ["E", "E", "a"]))]),
     ]
     failed = []
     for name, fn in checks:

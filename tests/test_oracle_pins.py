@@ -177,3 +177,62 @@ def test_tiny_workload_matches_hand_derivation():
     z1 = O.zigzag_rank_tokens(w.cu_padded, 2, 1).tolist()
     assert z0 == [0, 1, 6, 7, 8, 9, 10, 17, 18, 19, 20, 23]
     assert z1 == [2, 3, 4, 5, 11, 12, 13, 14, 15, 16, 21, 22]
+
+
+# ---- packing ("Packed Sequence 与上下文并行" §2.2, worked example §3.1-§3.4) ----
+
+def _encode(chars):
+    return [ord(c) for c in chars]
+
+
+PAD, EOD = ord("_"), ord("E")
+
+
+def test_pack_reproduces_the_worked_example(worked):
+    rows = [_encode(worked["sample0"]), _encode(worked["sample1"])]
+    align = int(worked["align_size"][0])
+    packed, cu_real, cu_pad = O.pack_batch(rows, PAD, EOD, align, 16, 3, ord("P"))
+    assert "".join(chr(v) for v in packed) == "".join(worked["tokens"])
+    assert cu_real[:4].tolist() == _ints(worked["cu_seqlens"])
+    assert cu_pad[:4].tolist() == _ints(worked["cu_seqlens_padded"])
+    # one trailing slot (empty here: the documents fill the budget exactly)
+    assert cu_real.tolist()[4:] == [13] and cu_pad.tolist()[4:] == [16]
+    _, mask = O.roll_labels(packed, cu_pad, cu_real, 16, 1)
+    assert mask[0].tolist() == _ints(worked["valid_mask"])
+
+
+def test_pack_budget_and_empty_slots():
+    # Room for 5 documents in 24 tokens: 3 documents (12 padded tokens), a
+    # trailing pad slot of 12, two empty slots.
+    rows = [_encode("abE_____"), _encode("cdeEf___")]
+    packed, cu_real, cu_pad = O.pack_batch(rows, PAD, EOD, 4, 24, 5, -1)
+    assert cu_real.tolist() == [0, 3, 7, 8, 8, 8, 8]
+    assert cu_pad.tolist() == [0, 4, 8, 12, 24, 24, 24]
+    assert packed.tolist()[:12] == _encode("abE") + [-1] + _encode("cdeE") + _encode("f") + [-1, -1, -1]
+    assert (packed[12:] == -1).all()
+
+
+@pytest.mark.parametrize("rows,want_docs", [
+    (["____"], []),                                   # an all-pad row has no document
+    (["a_bE__"], ["a_bE"]),                           # PAD inside the valid part stays in the document
+    (["abE"], ["abE"]),                               # a row ending in EOD: no empty trailing document
+    (["aEbc_"], ["aE", "bc"]),                        # the last document has no EOD
+    (["abcd"], ["abcd"]),                             # one document fills the row
+    (["EE_", "a__"], ["E", "E", "a"]),                # back-to-back EODs; rows stay separate
+])
+def test_pack_corner_cases(rows, want_docs):
+    packed, cu_real, cu_pad = O.pack_batch([_encode(r) for r in rows], PAD, EOD, 2, 32, 8, 0)
+    n = len(want_docs)
+    lens = [len(d) for d in want_docs]
+    assert np.diff(cu_real[:n + 1]).tolist() == lens
+    assert np.diff(cu_pad[:n + 1]).tolist() == [v + v % 2 for v in lens]
+    for k, d in enumerate(want_docs):
+        assert "".join(chr(v) for v in packed[cu_pad[k]:cu_pad[k] + len(d)]) == d
+
+
+@pytest.mark.parametrize("max_docs,capacity,kind", [(1, 16, "PACK_DOCS"), (3, 12, "PACK_CAPACITY")])
+def test_pack_overflow(worked, max_docs, capacity, kind):
+    rows = [_encode(worked["sample0"]), _encode(worked["sample1"])]
+    with pytest.raises(O.OracleInputError) as e:
+        O.pack_batch(rows, PAD, EOD, 4, capacity, max_docs, 0)
+    assert e.value.kind == kind

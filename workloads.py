@@ -229,3 +229,22 @@ def random_packed(seed, cp: int, n_docs: int, max_chunk: int, n_empty: int = 0,
     return Workload(f"random{seed}", 100, cp, cumulative(padded), cumulative(real), tuple(row_shape),
                     row_dtype=row_dtype, max_shift=1,
                     seed_extra=tuple(np.atleast_1d(seed).tolist()))
+
+
+def token_rows(seed, batch: int, seq: int, pad_id: int = 0, eod_id: int = 1, eod_rate: float = 0.01,
+               pad_tail_max: int | None = None, inner_pad_rate: float = 0.0) -> np.ndarray:
+    """Seeded [batch, seq] int64 token rows for packing tests: ids drawn from
+    [2, 32000), EOD tokens at rate ``eod_rate``, a PAD tail of up to
+    ``pad_tail_max`` tokens per row (whole rows of PAD possible), and PAD
+    tokens inside the valid part at rate ``inner_pad_rate``."""
+    rng = np.random.default_rng([BASE_SEED, 200, *np.atleast_1d(seed).tolist()])
+    rows = rng.integers(2, VOCAB, size=(batch, seq), dtype=np.int64)
+    rows[rng.random((batch, seq)) < eod_rate] = eod_id
+    if inner_pad_rate:
+        rows[rng.random((batch, seq)) < inner_pad_rate] = pad_id
+    tail_max = seq if pad_tail_max is None else pad_tail_max
+    for b in range(batch):
+        tail = int(rng.integers(0, tail_max, endpoint=True))
+        if tail:
+            rows[b, seq - tail:] = pad_id
+    return rows
