@@ -394,8 +394,7 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
 
 int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
                     int32_t tile_order) {
-  if (tile_bytes < 0 || max_workgroups < 0 || nontemporal < 0 || nontemporal > 1 || tile_order < 0 ||
-      tile_order > 2)
+  if (tile_bytes < 0 || max_workgroups < 0 || nontemporal < 0 || nontemporal > 1 || tile_order < 0)
     return THD_ERR_ARG;
   if (block_threads != 0 && block_threads != 128 && block_threads != 256 && block_threads != 512 &&
       block_threads != 1024)

@@ -66,7 +66,7 @@ struct SwapLaunch {
   int32_t max_workgroups;
   int32_t nontemporal;    // 1 on, 0 off
   int32_t block_threads;  // 128, 256, 512 or 1024
-  int32_t tile_order;     // 1 natural, 2 XCD-grouped
+  int32_t tile_order;     // tiles per XCD chunk: 1 natural order, G > 1 XCD-chunked
 };
 hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                        const void* in, void* out, int32_t total, int64_t row_bytes,

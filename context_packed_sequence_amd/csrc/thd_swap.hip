@@ -175,24 +175,26 @@ __global__ __launch_bounds__(BLOCK) void swap_small_kernel(const int32_t* __rest
   }
 }
 
-// Tile order.  Natural: workgroup b copies tile b.  XCD-grouped: the chip
-// hands workgroup b to XCD b mod 8, so tile (b mod 8) * ceil(n/8) + b / 8 gives
-// every XCD one contiguous eighth of the output, streamed front to back.
+// Tile order.  The chip hands workgroup b to XCD b mod 8.  Natural order
+// (chunk 1): workgroup b copies tile b, so consecutive tiles land on
+// different XCDs.  XCD-chunked order (chunk G): the tiles are cut into chunks
+// of G, XCD x takes chunks x, x + 8, x + 16, ... and walks each chunk front to
+// back, i.e. workgroup b = 8 j + x copies tile ((j / G) * 8 + x) * G + j mod G.
 constexpr int kXcds = 8;
 
-template <typename U, int BLOCK, int UNROLL, bool NT, bool XCD>
+template <typename U, int BLOCK, int UNROLL, bool NT>
 __global__ __launch_bounds__(BLOCK) void swap_kernel(const int32_t* __restrict__ hdr, int runs_word,
                                                      const RunPair* __restrict__ runs,
                                                      const DirEntry* __restrict__ dir,
                                                      const unsigned char* __restrict__ in,
                                                      unsigned char* __restrict__ out, int32_t total,
-                                                     int64_t row_bytes, int32_t tile_rows, int32_t n_tiles) {
+                                                     int64_t row_bytes, int32_t tile_rows, int32_t n_tiles,
+                                                     int32_t chunk, int32_t n_slots) {
   if (hdr[kHdrStatus] != THD_OK) return;  // a failed build writes nothing
   const int32_t n_runs = hdr[runs_word];
-  const int32_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
-  const int32_t n_slots = XCD ? per_xcd * kXcds : n_tiles;
   for (int32_t slot = blockIdx.x; slot < n_slots; slot += gridDim.x) {
-    const int32_t tile = XCD ? (slot % kXcds) * per_xcd + slot / kXcds : slot;
+    const int32_t x = slot % kXcds, j = slot / kXcds;
+    const int32_t tile = chunk == 1 ? slot : ((j / chunk) * kXcds + x) * chunk + j % chunk;
     if (tile >= n_tiles) continue;
     const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(tile) * tile_rows);
     const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + tile_rows));
@@ -265,26 +267,20 @@ int copy_unit(int64_t row_bytes, const void* in, const void* out) {
 }
 
 struct Shape {
-  int32_t tile_rows, n_tiles, grid;
+  int32_t tile_rows, n_tiles, chunk, n_slots, grid;
 };
 
 template <typename U, int BLOCK, int UNROLL>
 hipError_t launch_typed(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir, const void* in,
-                        void* out, int32_t total, int64_t row_bytes, const Shape& sh, bool nt, bool xcd,
-                        hipStream_t stream) {
+                        void* out, int32_t total, int64_t row_bytes, const Shape& sh, bool nt, hipStream_t stream) {
   const auto* i8 = static_cast<const unsigned char*>(in);
   auto* o8 = static_cast<unsigned char*>(out);
-#define THD_LAUNCH(NT_, X_)                                                                                      \
-  hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, NT_, X_>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr,       \
-                     runs_word, runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles)
-  if (nt) {
-    if (xcd) THD_LAUNCH(true, true);
-    else THD_LAUNCH(true, false);
-  } else {
-    if (xcd) THD_LAUNCH(false, true);
-    else THD_LAUNCH(false, false);
-  }
-#undef THD_LAUNCH
+  if (nt)
+    hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, true>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr, runs_word,
+                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots);
+  else
+    hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, false>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr, runs_word,
+                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots);
   return hipGetLastError();
 }
 
@@ -320,16 +316,14 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   }
 
   // Launch shape.  Measured on MI355X: the swap streams best when each
-  // workgroup copies about one row -- 4 KiB tiles of 128 threads for rows
-  // under 8 KiB; one row per workgroup in XCD-grouped order for rows of 8 KiB
-  // and more, 512 threads up to 4 GiB per buffer and 256 beyond (an empirical
-  // split: 256 wins by ~2 % on the 16 GiB 1M-token batch, 512 by ~1-2 % on
-  // 1-2 GiB batches).  Every field can be overridden for sweeps.
+  // workgroup copies about one row -- 4 KiB tiles of 128 threads in natural
+  // order for rows under 8 KiB; one row per 512-thread workgroup in
+  // XCD-chunked order (chunks of 64 tiles) for rows of 8 KiB and more.  Every
+  // field can be overridden for sweeps.
   const bool big_rows = unit == 16 && row_bytes >= 8192;
-  const bool huge = static_cast<int64_t>(total) * row_bytes >= (int64_t{4} << 30);
   const int64_t tile_bytes = cfg.tile_bytes > 0 ? cfg.tile_bytes : (big_rows ? row_bytes : (unit == 16 ? 4096 : 8192));
-  int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (big_rows ? (huge ? 256 : 512) : 128) : 256);
-  const bool xcd = cfg.tile_order == 2 || (cfg.tile_order == 0 && big_rows);
+  const int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (big_rows ? 512 : 128) : 256);
+  int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order : (big_rows ? 64 : 1);
 
   int64_t tile_rows = (tile_bytes + row_bytes - 1) / row_bytes;
   if (tile_rows < 1) tile_rows = 1;
@@ -337,12 +331,17 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   Shape sh;
   sh.tile_rows = static_cast<int32_t>(tile_rows);
   sh.n_tiles = static_cast<int32_t>((total + tile_rows - 1) / tile_rows);
-  const int64_t slots = xcd ? static_cast<int64_t>((sh.n_tiles + kXcds - 1) / kXcds) * kXcds : sh.n_tiles;
-  sh.grid = static_cast<int32_t>(slots);
+  const int64_t per_xcd = (sh.n_tiles + kXcds - 1) / kXcds;
+  if (chunk > per_xcd) chunk = per_xcd > 0 ? per_xcd : 1;  // one chunk per XCD at most
+  sh.chunk = static_cast<int32_t>(chunk);
+  const int64_t slots = chunk == 1 ? sh.n_tiles : (sh.n_tiles + kXcds * chunk - 1) / (kXcds * chunk) * kXcds * chunk;
+  if (slots > INT32_MAX) return hipErrorInvalidValue;
+  sh.n_slots = static_cast<int32_t>(slots);
+  sh.grid = sh.n_slots;
   if (cfg.max_workgroups > 0 && sh.grid > cfg.max_workgroups) sh.grid = cfg.max_workgroups;
   if (sh.grid <= 0) return hipSuccess;
   const bool nt = cfg.nontemporal != 0;
-#define THD_SWAP_ARGS hdr, runs, runs_word, dir, in, out, total, row_bytes, sh, nt, xcd, stream
+#define THD_SWAP_ARGS hdr, runs, runs_word, dir, in, out, total, row_bytes, sh, nt, stream
   switch (unit) {
     case 16:
       switch (block) {

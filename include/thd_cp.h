@@ -285,9 +285,12 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
  *   max_workgroups  cap on workgroups; above it workgroups loop over tiles
  *   nontemporal     1: non-temporal loads and stores (built-in), 0: plain
  *   block_threads   128, 256, 512 or 1024 for the 16-byte path
- *   tile_order      1: tile b to workgroup b; 2: XCD-grouped (each of the 8
- *                   XCDs streams one contiguous eighth of the output);
- *                   built-in: grouped for rows of 8 KiB and more
+ *   tile_order      tiles per XCD chunk: 1 = natural order (tile b to
+ *                   workgroup b, so neighbouring tiles go to different
+ *                   XCDs); G > 1 = XCD-chunked (tiles cut into chunks of G,
+ *                   XCD x streams chunks x, x+8, ...; G >= tiles / 8
+ *                   gives each XCD one contiguous eighth); built-in: 1
+ *                   for rows under 8 KiB, 64 otherwise
  * thd_swap_tuning(0, 0, 1, 0, 0) restores the built-in shape.
  */
 int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,

@@ -104,7 +104,7 @@ def test_host_rejections_without_device_work(pkg):
     assert lib.thd_swap_tuning(0, -1, 1, 0, 0) == pkg.THD_ERR_ARG
     assert lib.thd_swap_tuning(0, 0, 2, 0, 0) == pkg.THD_ERR_ARG
     assert lib.thd_swap_tuning(0, 0, 1, 300, 0) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, 0, 1, 0, 3) == pkg.THD_ERR_ARG
+    assert lib.thd_swap_tuning(0, 0, 1, 0, -1) == pkg.THD_ERR_ARG
     assert lib.thd_swap_tuning(0, 0, 1, 0, 0) == pkg.THD_OK
 
 

@@ -213,3 +213,31 @@ def test_calls_never_wait_for_the_gpu(thd):
     assert gate_ms > enqueue_s * 1e3
     assert torch.equal(b, x)
     assert int(status.item()) == 0
+
+
+def test_side_streams_and_two_routes(thd):
+    # Two routes built and used on two non-default streams, interleaved; each
+    # stream's work is ordered, the routes share nothing.
+    import torch
+    wa = W.random_packed(900, 4, 40, 30, 3, row_shape=(64,), row_dtype="uint8")
+    wb = W.random_packed(901, 8, 25, 20, 5, row_shape=(64,), row_dtype="uint8")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ra = thd.Route(wa.n_slots, wa.cp, wa.total)
+    rb = thd.Route(wb.n_slots, wb.cp, wb.total)
+    xa = torch.from_numpy(wa.rows_host()).cuda()
+    xb = torch.from_numpy(wb.rows_host()).cuda()
+    cua, cub = dev_i32(wa.cu_padded), dev_i32(wb.cu_padded)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sa):
+        ra.build(cua, wa.cp, wa.total, stream=sa.cuda_stream)
+        ya = ra.swap(xa, thd.Z2C, stream=sa.cuda_stream)
+    with torch.cuda.stream(sb):
+        rb.build(cub, wb.cp, wb.total, stream=sb.cuda_stream)
+        yb = rb.swap(xb, thd.C2Z, stream=sb.cuda_stream)
+    with torch.cuda.stream(sa):
+        za = ra.swap(ya, thd.C2Z, stream=sa.cuda_stream)
+    torch.cuda.synchronize()
+    assert ra.status(sa.cuda_stream) == 0 and rb.status(sb.cuda_stream) == 0
+    assert np.array_equal(ya.cpu().numpy(), O.swap_rows(wa.rows_host(), wa.cu_padded, wa.cp, wa.total, "z2c"))
+    assert np.array_equal(yb.cpu().numpy(), O.swap_rows(wb.rows_host(), wb.cu_padded, wb.cp, wb.total, "c2z"))
+    assert torch.equal(za, xa)
