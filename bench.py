@@ -75,6 +75,97 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def _median_event_ms(torch, stream, fn, reps):
+    evs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2]
+
+
+def measure_next(thd, torch, workloads, w, route, x, stream, step_on, reps=20):
+    """The widened rows on the same batch: one-launch multi-key slice, roll
+    written in zigzag order, device packing, and a graph-captured step."""
+    T, dev, sh = w.total, x.device, stream.cuda_stream
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(workloads.BASE_SEED + 77)
+    keys = [torch.randint(0, 32000, (T,), dtype=torch.int64, device=dev, generator=g) for _ in range(3)]
+    keys += [torch.randint(0, 2, (T,), dtype=torch.uint8, device=dev, generator=g) for _ in range(2)]
+    outs = [torch.empty_like(k) for k in keys]
+    rbs = [k.element_size() for k in keys]
+    for _ in range(3):
+        thd.thd_swap_batch(route.handle, thd.C2Z, keys, outs, rbs, T, sh)
+    t_batch = _median_event_ms(torch, stream, lambda: thd.thd_swap_batch(route.handle, thd.C2Z, keys, outs, rbs, T, sh),
+                               reps)
+
+    def separate():
+        for k, o, r in zip(keys, outs, rbs):
+            thd.thd_swap(route.handle, thd.C2Z, k, o, T, r, sh)
+    t_sep = _median_event_ms(torch, stream, separate, reps)
+    moved = 2 * T * sum(rbs)
+    out["multi_key_swap"] = {"keys": "3 x int64 + 2 x uint8 per token", "us": round(t_batch * 1e3, 2),
+                             "gbps": round(moved / (t_batch * 1e-3) / 1e9, 1),
+                             "five_thd_swap_calls_us": round(t_sep * 1e3, 2)}
+
+    cu = torch.from_numpy(w.cu_padded).to(dev)
+    cu_real = torch.from_numpy(w.cu_real).to(dev)
+    j = max(w.max_shift, 1)
+    shifted = torch.empty((j, T), dtype=torch.int64, device=dev)
+    mask = torch.empty((j + 1, T), dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    ids = keys[0]
+    t_rz = _median_event_ms(torch, stream, lambda: thd.thd_roll_labels_zigzag(
+        route.handle, ids, cu, cu_real, w.n_slots, T, j, 0, shifted, mask, status, sh), reps)
+    t_rn = _median_event_ms(torch, stream, lambda: thd.thd_roll_labels(
+        ids, cu, cu_real, w.n_slots, T, j, 0, shifted, mask, status, sh), reps)
+    out["roll_zigzag_us"] = round(t_rz * 1e3, 2)
+    out["roll_natural_us"] = round(t_rn * 1e3, 2)
+
+    batch = 16
+    seq = T // batch
+    align = 2 * w.cp
+    max_docs = 256
+    rows = torch.from_numpy(workloads.token_rows(7, batch, seq, 0, 1, 1.0 / 4096, 512)).to(dev)
+    capacity = ((batch * seq) // align + max_docs + 1) * align
+    nbytes = thd.thd_pack_workspace_bytes(batch, seq)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    packed = torch.empty(capacity, dtype=torch.int64, device=dev)
+    pcu = torch.empty(max_docs + 2, dtype=torch.int32, device=dev)
+    pcup = torch.empty(max_docs + 2, dtype=torch.int32, device=dev)
+    pst = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def do_pack():
+        thd.thd_pack(rows, batch, seq, 0, 1, align, capacity, max_docs, 0, ws, nbytes, packed, pcu, pcup, pst, sh)
+    do_pack()
+    t_pack = _median_event_ms(torch, stream, do_pack, reps)
+    assert int(pst.item()) == 0
+    pack_bytes = 8 * batch * seq + 8 * capacity
+    out["pack"] = {"rows": f"[{batch},{seq}] int64", "capacity": capacity, "us": round(t_pack * 1e3, 2),
+                   "gbps": round(pack_bytes / (t_pack * 1e-3) / 1e9, 1)}
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step_on(side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step_on(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    graph.replay()
+    t_graph = _median_event_ms(torch, stream, graph.replay, reps)
+    t_eager = _median_event_ms(torch, stream, lambda: step_on(sh), reps)
+    out["graph_step_ms"] = round(t_graph, 4)
+    out["eager_step_ms"] = round(t_eager, 4)
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -250,6 +341,15 @@ def main():
         copy_ms.append(c0.elapsed_time(c1))
     copy_gbps = swap_bytes / (float(np.median(copy_ms)) * 1e-3) / 1e9
 
+    def step_on(s):
+        thd.thd_build_route(h, cu, n_slots, cp, total, s)
+        for _ in range(layers):
+            thd.thd_swap(h, thd.Z2C, x, a, total, rb, s)
+            thd.thd_swap(h, thd.C2Z, a, b, total, rb, s)
+        thd.thd_roll_labels(ids, cu, cu_real, n_slots, total, j, 0, shifted, mask, status, s)
+
+    next_rows = measure_next(thd, torch, workloads, w, route, x, stream, step_on)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = oracle_baseline(w, layers, args.cpu_seconds)
@@ -295,6 +395,7 @@ def main():
             "traffic": measured_traffic(w.name),
         },
         "cpu_baseline": cpu,
+        "next": next_rows,
     }
     print(json.dumps(out), flush=True)
     route.close()
