@@ -112,6 +112,34 @@ def measure_next(thd, torch, workloads, w, route, x, stream, step_on, reps=20):
                              "gbps": round(moved / (t_batch * 1e-3) / 1e9, 1),
                              "five_thd_swap_calls_us": round(t_sep * 1e3, 2)}
 
+    # the tensors of one gated-delta-net layer (q, k, v with the activation's
+    # row shape, then the decay gate g in fp32 and beta in bf16 per head)
+    # through the route in one launch, against one thd_swap per tensor
+    heads = 16
+    layer_in = [torch.empty_like(x) for _ in range(3)]
+    layer_in += [torch.empty((T, heads), dtype=torch.float32, device=dev),
+                 torch.empty((T, heads), dtype=torch.bfloat16, device=dev)]
+    for t in layer_in:
+        t.view(torch.uint8).random_(0, 256, generator=g)
+    layer_out = [torch.empty_like(t) for t in layer_in]
+    layer_rb = [t.numel() // T * t.element_size() for t in layer_in]
+    for _ in range(3):
+        thd.thd_swap_batch(route.handle, thd.Z2C, layer_in, layer_out, layer_rb, T, sh)
+    t_layer = _median_event_ms(torch, stream, lambda: thd.thd_swap_batch(route.handle, thd.Z2C, layer_in,
+                                                                          layer_out, layer_rb, T, sh), reps)
+
+    def layer_separate():
+        for i_, o_, r_ in zip(layer_in, layer_out, layer_rb):
+            thd.thd_swap(route.handle, thd.Z2C, i_, o_, T, r_, sh)
+    t_layer_sep = _median_event_ms(torch, stream, layer_separate, reps)
+    layer_moved = 2 * T * sum(layer_rb)
+    out["layer_batch_swap"] = {"tensors": f"q,k,v {list(x.shape[1:])} bf16 + g [{heads}] fp32 + beta [{heads}] bf16",
+                               "row_bytes": layer_rb, "us": round(t_layer * 1e3, 2),
+                               "gbps": round(layer_moved / (t_layer * 1e-3) / 1e9, 1),
+                               "separate_calls_us": round(t_layer_sep * 1e3, 2),
+                               "separate_gbps": round(layer_moved / (t_layer_sep * 1e-3) / 1e9, 1)}
+    del layer_in, layer_out
+
     cu = torch.from_numpy(w.cu_padded).to(dev)
     cu_real = torch.from_numpy(w.cu_real).to(dev)
     j = max(w.max_shift, 1)
@@ -330,16 +358,15 @@ def main():
     host_syncs = 0 if not gate.query() else None
     torch.cuda.synchronize()
 
-    # context: a plain device-to-device copy of the same bytes
-    copy_ms = []
-    for _ in range(10):
-        c0, c1 = ev(), ev()
-        c0.record(stream)
-        a.copy_(x)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        copy_ms.append(c0.elapsed_time(c1))
-    copy_gbps = swap_bytes / (float(np.median(copy_ms)) * 1e-3) / 1e9
+    # ceilings in the same run: the runtime's device-to-device copy (torch
+    # copy_ of the same activation) and the library's plain streaming copy
+    # (the swap's units and workgroup shape without the route)
+    nbytes = total * rb
+    copy_dtod_ms = _median_event_ms(torch, stream, lambda: a.copy_(x), 20)
+    thd.thd_copy(x, a, nbytes, s_handle)
+    copy_stream_ms = _median_event_ms(torch, stream, lambda: thd.thd_copy(x, a, nbytes, s_handle), 20)
+    copy_gbps = swap_bytes / (copy_dtod_ms * 1e-3) / 1e9
+    stream_copy_gbps = swap_bytes / (copy_stream_ms * 1e-3) / 1e9
 
     def step_on(s):
         thd.thd_build_route(h, cu, n_slots, cp, total, s)
@@ -385,7 +412,10 @@ def main():
         "route_build_enqueue_us": round(float(np.median(enq)) * 1e6, 2),
         "roll_us": round(float(np.median(roll_ms)) * 1e3, 2),
         "host_syncs": host_syncs,
-        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "swap_us_by_direction": {
+            d: {"median": round(float(np.median(v)) * 1e3, 2), "min": round(float(np.min(v)) * 1e3, 2)}
+            for d, v in (("z2c", swap_ms[0::2]), ("c2z", swap_ms[1::2]))},
+        "copy_ceiling_gbps": {"dtod_copy": round(copy_gbps, 1), "stream_copy": round(stream_copy_gbps, 1)},
         "roofline": {
             "bound": "hbm",
             "achieved": round(swap_gbps, 1),

@@ -39,6 +39,7 @@ from .binding import (  # noqa: F401
     THD_ZIGZAG_TO_CONTIGUOUS,
     ThdError,
     thd_build_route,
+    thd_copy,
     thd_pack,
     thd_pack_workspace_bytes,
     thd_roll_labels,

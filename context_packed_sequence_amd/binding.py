@@ -49,7 +49,7 @@ THD_MAX_BATCH = 16
 EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",
     "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_swap_tuning", "thd_strerror",
-    "thd_swap_batch", "thd_roll_labels_zigzag", "thd_pack_workspace_bytes", "thd_pack",
+    "thd_swap_batch", "thd_roll_labels_zigzag", "thd_pack_workspace_bytes", "thd_pack", "thd_copy",
 )
 
 
@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "thd_roll_labels_zigzag": (ctypes.c_int, [c_p, c_p, c_p, c_p, c_i32, c_i64, c_i32, c_i64, c_p, c_p, c_p,
                                                   c_p]),
         "thd_pack_workspace_bytes": (ctypes.c_int64, [c_i32, c_i32]),
+        "thd_copy": (ctypes.c_int, [c_p, c_p, c_i64, c_p]),
         "thd_pack": (ctypes.c_int, [c_p, c_i32, c_i32, c_i64, c_i64, c_i32, c_i64, c_i32, c_i64, c_p, c_i64, c_p,
                                     c_p, c_p, c_p, c_p]),
     }
@@ -188,6 +189,10 @@ def thd_pack(tokens, batch: int, seq: int, pad_id: int, eod_id: int, align: int,
     return _check(_lib.thd_pack(_ptr(tokens), batch, seq, pad_id, eod_id, align, capacity, max_docs, pad_value,
                                 _ptr(workspace), workspace_bytes, _ptr(packed), _ptr(cu_seqlens),
                                 _ptr(cu_seqlens_padded), _ptr(status), _stream(stream)), "thd_pack")
+
+
+def thd_copy(x, out, nbytes: int, stream=None) -> int:
+    return _check(_lib.thd_copy(_ptr(x), _ptr(out), nbytes, _stream(stream)), "thd_copy")
 
 
 def thd_route_status(route: int, stream=None) -> int:

@@ -193,6 +193,15 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
   return THD_OK;
 }
 
+int thd_copy(const void* in, void* out, int64_t bytes, void* stream) {
+  if (bytes < 0) return THD_ERR_ARG;
+  if (bytes == 0) return THD_OK;
+  if (!in || !out) return THD_ERR_ARG;
+  if (overlaps(in, bytes, out, bytes)) return THD_ERR_ALIAS;
+  if (thdcp::launch_copy(in, out, bytes, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
+  return THD_OK;
+}
+
 int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const int32_t* cu_seqlens, int32_t n_slots,
                     int64_t total_tokens, int32_t max_shift, int64_t fill, int64_t* shifted, uint8_t* mask,
                     int32_t* status, void* stream) {

@@ -72,6 +72,7 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
                        const void* in, void* out, int32_t total, int64_t row_bytes,
                        const SwapLaunch& cfg, hipStream_t stream);
 
+hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t stream);
 hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                              int32_t n, const void* const* ins, void* const* outs, const int64_t* row_bytes,
                              int32_t total, hipStream_t stream);

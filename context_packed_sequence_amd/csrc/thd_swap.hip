@@ -96,6 +96,30 @@ __device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, cons
   }
 }
 
+// Part of one output row: bytes [b0, b1) of row r, for rows so long that a
+// workgroup takes a slice of a row rather than whole rows.
+template <typename U, int BLOCK, int UNROLL, bool NT>
+__device__ __forceinline__ void swap_row_part(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
+                                              int32_t n_runs, const unsigned char* __restrict__ in,
+                                              unsigned char* __restrict__ out, int64_t row_bytes, int32_t r,
+                                              int64_t b0, int64_t b1) {
+  const DirEntry e = dir[r >> kDirShift];
+  int32_t in_row;
+  if (r < e.run_end) {
+    in_row = e.in + (r & (kDirBlock - 1));
+  } else {
+    int32_t k = e.run + 1;
+    while (k + 1 < n_runs && runs[k + 1].out <= r) ++k;
+    if (k >= n_runs) return;
+    const RunPair run = runs[k];
+    if (run.out > r) return;
+    in_row = run.in + (r - run.out);
+  }
+  const U* src = reinterpret_cast<const U*>(in + static_cast<int64_t>(in_row) * row_bytes + b0);
+  U* dst = reinterpret_cast<U*>(out + static_cast<int64_t>(r) * row_bytes + b0);
+  copy_span<U, BLOCK, UNROLL, NT>(src, dst, (b1 - b0) / static_cast<int64_t>(sizeof(U)));
+}
+
 // Small rows (row_bytes equal to the copy unit, at most 16 B: token ids,
 // labels, masks, position ids): copying run piece by run piece would leave
 // most lanes idle on short pieces, so the tile's runs are staged in LDS and
@@ -213,7 +237,8 @@ struct BatchTensor {
   int32_t tile_rows;
   int32_t first_tile;  // index of the tensor's first tile in the launch
   int32_t unit;        // copy unit in bytes: 16, 8, 4, 2 or 1
-  int32_t pad;
+  int32_t parts;       // > 1: each tile is one part of one row, part_bytes long
+  int64_t part_bytes;
 };
 
 struct BatchArgs {
@@ -222,9 +247,9 @@ struct BatchArgs {
   int32_t total_tiles;
 };
 
-constexpr int kBatchBlock = 256;
+constexpr int kBatchBlock = 128;
 
-__global__ __launch_bounds__(kBatchBlock) void swap_batch_kernel(const int32_t* __restrict__ hdr, int runs_word,
+__global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))) void swap_batch_kernel(const int32_t* __restrict__ hdr, int runs_word,
                                                                  const RunPair* __restrict__ runs,
                                                                  const DirEntry* __restrict__ dir, int32_t total,
                                                                  BatchArgs args) {
@@ -236,11 +261,18 @@ __global__ __launch_bounds__(kBatchBlock) void swap_batch_kernel(const int32_t* 
     int i = 0;
     while (i + 1 < args.n && args.t[i + 1].first_tile <= g) ++i;
     const BatchTensor bt = args.t[i];
+    if (bt.parts > 1) {  // long rows (16-byte units only): one slice of one row per tile
+      const int32_t r = (g - bt.first_tile) / bt.parts;
+      const int64_t b0 = static_cast<int64_t>((g - bt.first_tile) % bt.parts) * bt.part_bytes;
+      const int64_t b1 = min(bt.row_bytes, b0 + bt.part_bytes);
+      swap_row_part<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, bt.row_bytes, r, b0, b1);
+      continue;
+    }
     const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(g - bt.first_tile) * bt.tile_rows);
     const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + bt.tile_rows));
     if (bt.row_bytes == bt.unit) {  // one unit per row: the LDS-staged small-row path
       switch (bt.unit) {
-        case 16: swap_tile_small<u32x4, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
+        case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, 16, r0, r1); break;
         case 8: swap_tile_small<u32x2, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
         case 4: swap_tile_small<uint32_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
         case 2: swap_tile_small<uint16_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
@@ -249,13 +281,26 @@ __global__ __launch_bounds__(kBatchBlock) void swap_batch_kernel(const int32_t* 
       continue;
     }
     switch (bt.unit) {
-      case 16: swap_tile<u32x4, kBatchBlock, 4, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
       case 8: swap_tile<u32x2, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
       case 4: swap_tile<uint32_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
       case 2: swap_tile<uint16_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
       default: swap_tile<uint8_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
     }
   }
+}
+
+// Plain streaming copy of whole tiles: no route, no permutation.  The same
+// units, workgroup shape and non-temporal accesses as the swap's streaming
+// path, so a swap can be compared with a copy of the same bytes.
+template <typename U, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void copy_kernel(const unsigned char* __restrict__ in,
+                                                     unsigned char* __restrict__ out, int64_t bytes,
+                                                     int64_t tile_bytes) {
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * tile_bytes;
+  if (b0 >= bytes) return;
+  const int64_t n = min(tile_bytes, bytes - b0) / static_cast<int64_t>(sizeof(U));
+  copy_span<U, BLOCK, UNROLL, true>(reinterpret_cast<const U*>(in + b0), reinterpret_cast<U*>(out + b0), n);
 }
 
 int copy_unit(int64_t row_bytes, const void* in, const void* out) {
@@ -371,19 +416,50 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
                                              : (tile_bytes + row_bytes[i] - 1) / row_bytes[i];
     if (tile_rows < 1) tile_rows = 1;
     if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
+    // rows longer than a tile (16-byte units): every workgroup still moves
+    // about 4 KiB, a slice of one row
+    int64_t parts = 1, part_bytes = row_bytes[i];
+    if (unit == 16 && row_bytes[i] > tile_bytes) {
+      parts = (row_bytes[i] + tile_bytes - 1) / tile_bytes;
+      part_bytes = ((row_bytes[i] + parts - 1) / parts + 15) / 16 * 16;
+      parts = (row_bytes[i] + part_bytes - 1) / part_bytes;
+      if (parts > INT32_MAX) return hipErrorInvalidValue;
+    }
     args.t[i].in = static_cast<const unsigned char*>(ins[i]);
     args.t[i].out = static_cast<unsigned char*>(outs[i]);
     args.t[i].row_bytes = row_bytes[i];
     args.t[i].tile_rows = static_cast<int32_t>(tile_rows);
     args.t[i].first_tile = static_cast<int32_t>(tiles);
     args.t[i].unit = unit;
-    tiles += (total + tile_rows - 1) / tile_rows;
+    args.t[i].parts = static_cast<int32_t>(parts);
+    args.t[i].part_bytes = part_bytes;
+    tiles += parts > 1 ? static_cast<int64_t>(total) * parts : (total + tile_rows - 1) / tile_rows;
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
   }
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   args.total_tiles = static_cast<int32_t>(tiles);
   hipLaunchKernelGGL(swap_batch_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kBatchBlock), 0, stream, hdr,
                      runs_word, runs, dir, total, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t stream) {
+  const int unit = copy_unit(bytes, in, out);
+  const int64_t tile_bytes = unit == 16 ? 4096 : 8192;
+  const int64_t tiles = (bytes + tile_bytes - 1) / tile_bytes;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  const auto* i8 = static_cast<const unsigned char*>(in);
+  auto* o8 = static_cast<unsigned char*>(out);
+  const dim3 grid(static_cast<unsigned>(tiles));
+  switch (unit) {
+    case 16: hipLaunchKernelGGL((copy_kernel<u32x4, 128, 8>), grid, dim3(128), 0, stream, i8, o8, bytes, tile_bytes); break;
+    case 8: hipLaunchKernelGGL((copy_kernel<u32x2, 256, 4>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
+    case 4: hipLaunchKernelGGL((copy_kernel<uint32_t, 256, 8>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
+    case 2: hipLaunchKernelGGL((copy_kernel<uint16_t, 256, 8>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
+    default: hipLaunchKernelGGL((copy_kernel<uint8_t, 256, 8>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
+  }
   return hipGetLastError();
 }
 

@@ -296,6 +296,17 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
 int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
                     int32_t tile_order);
 
+/*
+ * thd_copy -- plain streaming copy of `bytes` bytes from `in` to `out`
+ * (device pointers, non-overlapping): no route, no permutation.  It moves
+ * the bytes with the same 16-byte non-temporal units and workgroup shape as
+ * thd_swap, so a swap's bandwidth can be set beside that of a copy of the
+ * same bytes in the same run.  Stream-ordered, one launch; THD_ERR_ARG for a
+ * negative size or a null pointer (bytes > 0), THD_ERR_ALIAS for overlapping
+ * buffers; 0 bytes is THD_OK with no launch.
+ */
+int thd_copy(const void* in, void* out, int64_t bytes, void* stream);
+
 /* thd_strerror -- static text for a return or status code. */
 const char* thd_strerror(int32_t code);
 

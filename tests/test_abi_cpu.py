@@ -99,6 +99,11 @@ def test_host_rejections_without_device_work(pkg):
     assert pack(batch=-1) == pkg.THD_ERR_ARG
     assert pack(cu=(1 << 31) + 8) == pkg.THD_ERR_ALIAS
     assert pack(packed=(1 << 20) + 64) == pkg.THD_ERR_ALIAS
+    # plain copy: negative size, null pointers, overlap; zero bytes launches nothing
+    assert lib.thd_copy(1 << 20, 1 << 24, -1, None) == pkg.THD_ERR_ARG
+    assert lib.thd_copy(None, 1 << 24, 16, None) == pkg.THD_ERR_ARG
+    assert lib.thd_copy(1 << 20, (1 << 20) + 8, 16, None) == pkg.THD_ERR_ALIAS
+    assert lib.thd_copy(None, None, 0, None) == pkg.THD_OK
     # tuning argument checks
     assert lib.thd_swap_tuning(-1, 0, 1, 0, 0) == pkg.THD_ERR_ARG
     assert lib.thd_swap_tuning(0, -1, 1, 0, 0) == pkg.THD_ERR_ARG

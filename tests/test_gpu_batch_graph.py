@@ -40,7 +40,9 @@ def batch_keys(w, rng):
         "position_ids": rng.integers(0, 65536, size=t, dtype=np.int64),
         "valid_mask": rng.integers(0, 2, size=t, dtype=np.uint8),
         "fp32_pair": rng.standard_normal((t, 2), dtype=np.float32),
+        "int64_pair": rng.integers(-2 ** 62, 2 ** 62, size=(t, 2), dtype=np.int64),   # one 16-byte unit per row
         "hidden": w.rows_host().view(np.int16),      # bf16 bit patterns
+        "wide": rng.integers(0, 256, size=(t, 4624), dtype=np.uint8),   # rows split into two slices
     }
 
 
@@ -74,6 +76,7 @@ def test_swap_batch_full_workload(thd):
     rng = np.random.default_rng(9)
     keys = batch_keys(w, rng)
     keys.pop("hidden")
+    keys.pop("wide")
     xs = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in keys.values()]
     pads = []
     outs = []

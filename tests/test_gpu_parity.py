@@ -247,3 +247,20 @@ def test_small_rows_with_dense_runs(thd, seed, cp, rb):
         out = route.swap(x, d)
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), O.swap_rows(w.rows_host(), cu, cp, total, direction)), direction
+
+
+@pytest.mark.parametrize("nbytes,offset", [(1 << 20, 0), (4096 * 37 + 16, 0), (1000, 8), (999, 4), (4098, 2),
+                                           (12345, 1), (3, 0)])
+def test_plain_copy(thd, nbytes, offset):
+    # The calibration copy: every unit width (16/8/4/2/1 B from the size and
+    # the pointers' alignment) and a ragged last tile; the guard bytes around
+    # the destination must stay untouched.
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda", generator=g)
+    dst = torch.full((nbytes + 64,), 7, dtype=torch.uint8, device="cuda")
+    say("copy", nbytes, offset)
+    assert thd.thd_copy(src[offset:offset + nbytes], dst[offset:offset + nbytes], nbytes) == thd.THD_OK
+    torch.cuda.synchronize()
+    assert torch.equal(dst[offset:offset + nbytes], src[offset:offset + nbytes])
+    assert (dst[:offset] == 7).all() and (dst[offset + nbytes:] == 7).all()
