@@ -33,6 +33,7 @@ from .binding import (  # noqa: F401
     THD_ERR_SHAPE,
     THD_IDENTITY,
     THD_MAX_BATCH,
+    THD_PACK_MAX_SEQ,
     THD_MAX_CP,
     THD_MAX_SHIFT,
     THD_OK,

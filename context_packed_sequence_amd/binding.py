@@ -45,6 +45,7 @@ THD_CONTIGUOUS_TO_ZIGZAG = 1
 THD_MAX_CP = 1024
 THD_MAX_SHIFT = 8
 THD_MAX_BATCH = 16
+THD_PACK_MAX_SEQ = 2147479552
 
 EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",

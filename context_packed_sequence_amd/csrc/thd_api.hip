@@ -265,20 +265,24 @@ int thd_swap_batch(const thd_route* route, int32_t direction, int32_t n_tensors,
 namespace {
 
 struct PackLayout {
-  int64_t hdr, ends, row_valid, row_docs, row_padded, row_doc_off, row_real_off, row_pack_off, bytes;
+  int64_t hdr, ch_lnp, ch_ne, ch_fe, ch_le, ch_ps, ch_prev, ch_doc_base, ch_pack_base, row_valid, row_real_off, bytes;
 };
 
-PackLayout pack_layout(int64_t batch, int64_t seq) {
+PackLayout pack_layout(int32_t batch, int32_t seq) {
+  const int64_t nc = thdcp::pack_chunks(batch, seq);
   PackLayout l{};
   int64_t off = 0;
   l.hdr = off;          off = align_up(off + 64, 256);
-  l.ends = off;         off = align_up(off + batch * seq * 4, 256);
-  l.row_valid = off;    off = align_up(off + batch * 4, 256);
-  l.row_docs = off;     off = align_up(off + batch * 4, 256);
-  l.row_padded = off;   off = align_up(off + batch * 8, 256);
-  l.row_doc_off = off;  off = align_up(off + batch * 8, 256);
-  l.row_real_off = off; off = align_up(off + batch * 8, 256);
-  l.row_pack_off = off; off = align_up(off + batch * 8, 256);
+  l.ch_lnp = off;       off = align_up(off + nc * 4, 256);
+  l.ch_ne = off;        off = align_up(off + nc * 4, 256);
+  l.ch_fe = off;        off = align_up(off + nc * 4, 256);
+  l.ch_le = off;        off = align_up(off + nc * 4, 256);
+  l.ch_ps = off;        off = align_up(off + nc * 8, 256);
+  l.ch_prev = off;      off = align_up(off + nc * 4, 256);
+  l.ch_doc_base = off;  off = align_up(off + nc * 8, 256);
+  l.ch_pack_base = off; off = align_up(off + nc * 8, 256);
+  l.row_valid = off;    off = align_up(off + static_cast<int64_t>(batch) * 4, 256);
+  l.row_real_off = off; off = align_up(off + static_cast<int64_t>(batch) * 8, 256);
   l.bytes = off;
   return l;
 }
@@ -286,14 +290,14 @@ PackLayout pack_layout(int64_t batch, int64_t seq) {
 }  // namespace
 
 int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq) {
-  if (batch < 0 || seq < 0) return -1;
+  if (batch < 0 || seq < 0 || seq > THD_PACK_MAX_SEQ) return -1;
   return pack_layout(batch, seq).bytes;
 }
 
 int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id, int32_t align,
              int64_t capacity, int32_t max_docs, int64_t pad_value, void* workspace, int64_t workspace_bytes,
              int64_t* packed, int32_t* cu_seqlens, int32_t* cu_seqlens_padded, int32_t* status, void* stream) {
-  if (batch < 0 || seq < 0 || align < 1 || capacity < 0 || capacity > INT32_MAX || capacity % align != 0 ||
+  if (batch < 0 || seq < 0 || seq > THD_PACK_MAX_SEQ || align < 1 || capacity < 0 || capacity > INT32_MAX || capacity % align != 0 ||
       max_docs < 0 || max_docs > INT32_MAX - 2 || pad_id == eod_id)
     return THD_ERR_ARG;
   const int64_t n_tok = static_cast<int64_t>(batch) * seq;
@@ -314,13 +318,16 @@ int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, 
   char* w = static_cast<char*>(workspace);
   thdcp::PackWs ws;
   ws.hdr = reinterpret_cast<int32_t*>(w + l.hdr);
-  ws.ends = reinterpret_cast<int32_t*>(w + l.ends);
+  ws.ch_lnp = reinterpret_cast<int32_t*>(w + l.ch_lnp);
+  ws.ch_ne = reinterpret_cast<int32_t*>(w + l.ch_ne);
+  ws.ch_fe = reinterpret_cast<int32_t*>(w + l.ch_fe);
+  ws.ch_le = reinterpret_cast<int32_t*>(w + l.ch_le);
+  ws.ch_ps = reinterpret_cast<int64_t*>(w + l.ch_ps);
+  ws.ch_prev = reinterpret_cast<int32_t*>(w + l.ch_prev);
+  ws.ch_doc_base = reinterpret_cast<int64_t*>(w + l.ch_doc_base);
+  ws.ch_pack_base = reinterpret_cast<int64_t*>(w + l.ch_pack_base);
   ws.row_valid = reinterpret_cast<int32_t*>(w + l.row_valid);
-  ws.row_docs = reinterpret_cast<int32_t*>(w + l.row_docs);
-  ws.row_padded = reinterpret_cast<int64_t*>(w + l.row_padded);
-  ws.row_doc_off = reinterpret_cast<int64_t*>(w + l.row_doc_off);
   ws.row_real_off = reinterpret_cast<int64_t*>(w + l.row_real_off);
-  ws.row_pack_off = reinterpret_cast<int64_t*>(w + l.row_pack_off);
   if (thdcp::launch_pack(tokens, batch, seq, pad_id, eod_id, align, static_cast<int32_t>(capacity), max_docs,
                          pad_value, ws, packed, cu_seqlens, cu_seqlens_padded, status, as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;

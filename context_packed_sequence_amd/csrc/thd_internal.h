@@ -91,15 +91,24 @@ hipError_t launch_roll(const int64_t* ids, const int32_t* cu_pad, const int32_t*
 
 // Views into the caller's packing workspace (see thd_pack_workspace_bytes).
 struct PackWs {
-  int32_t* hdr;          // [0] status, [1] documents, [2] padded tokens
-  int32_t* ends;         // [batch][seq] document ends per row (exclusive, row coordinates)
-  int32_t* row_valid;    // [batch] valid end of each row (= its real tokens)
-  int32_t* row_docs;     // [batch]
-  int64_t* row_padded;   // [batch] padded tokens of the row's documents
-  int64_t* row_doc_off;  // [batch] exclusive prefix sums over rows
-  int64_t* row_real_off;
-  int64_t* row_pack_off;
+  int32_t* hdr;           // [0] status, [1] documents, [2] padded tokens
+  // per chunk of a row (batch-major), from the chunk pass
+  int32_t* ch_lnp;        // last non-PAD position + 1 inside the chunk (row coordinates), 0: none
+  int32_t* ch_ne;         // EOD tokens in the chunk
+  int32_t* ch_fe;         // end (position + 1) of the chunk's first EOD, 0: none
+  int32_t* ch_le;         // end of the chunk's last EOD, 0: none
+  int64_t* ch_ps;         // padded lengths of the documents that start and end in the chunk
+  // per chunk, from the scan pass
+  int32_t* ch_prev;       // end of the last document of the row closed before the chunk
+  int64_t* ch_doc_base;   // index of the first document that ends in or after the chunk
+  int64_t* ch_pack_base;  // packed position where the document holding the chunk's first token starts
+  // per row, from the scan pass
+  int32_t* row_valid;     // valid end (last non-PAD position + 1)
+  int64_t* row_real_off;  // valid tokens of the earlier rows
 };
+
+// Chunks the pack kernels cut a [batch, seq] batch into.
+int64_t pack_chunks(int32_t batch, int32_t seq);
 
 hipError_t launch_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id,
                        int32_t align, int32_t capacity, int32_t max_docs, int64_t pad_value, const PackWs& ws,

@@ -16,95 +16,148 @@
 // one trailing pad-only slot and unused slots repeat the last boundary.  So
 // every shape the route build, the swaps and the roll need is known on the
 // host before the data is.
+//
+// Work decomposition: every row is cut into chunks of kChunk tokens and each
+// chunk is one workgroup, so a batch of a few long rows still fills the chip.
+//  * chunk pass: per chunk, the last non-PAD position, the number of EODs, the
+//    first and last EOD, and the padded lengths of the documents that start
+//    and end inside the chunk;
+//  * scan pass (one workgroup): scans over all chunks in batch order give
+//    each chunk the end of the last document closed before it, its first
+//    document index and the packed position of the document it starts in;
+//    the row sums give the trailing document of each row, and the totals
+//    give the budget checks;
+//  * write pass: per chunk, the tokens go to their packed positions, each
+//    document end writes its two boundaries, and the chunk's pads are spread
+//    over all its threads.
 #include "thd_device.h"
 #include "thd_internal.h"
 
 namespace thdcp {
 namespace {
 
-constexpr int kPackThreads = 1024;
-constexpr int kPackWaves = kPackThreads / 64;
+constexpr int kChunk = 1024;          // tokens per chunk (one workgroup)
+constexpr int kChunkThreads = 256;
+constexpr int kPer = kChunk / kChunkThreads;  // consecutive tokens per thread
+constexpr int kScanThreads = 1024;
 
-// Rows: valid end, document ends (exclusive, row coordinates) and the row's
-// padded token count.
-__global__ __launch_bounds__(kPackThreads) void pack_rows_kernel(const int64_t* __restrict__ tokens, int32_t seq,
-                                                                 int64_t pad_id, int64_t eod_id, int32_t align,
-                                                                 PackWs ws) {
-  __shared__ int s_wave[kPackWaves + 1];
-  __shared__ int64_t s_wave64[kPackWaves + 1];
-  __shared__ int s_valid, s_cnt;
+__device__ __forceinline__ int64_t padded_len(int64_t len, int32_t align) {
+  return len + (align - len % align) % align;
+}
+
+// Chunk pass.
+__global__ __launch_bounds__(kChunkThreads) void pack_chunks_kernel(const int64_t* __restrict__ tokens, int32_t seq,
+                                                                    int32_t n_ch, int64_t pad_id, int64_t eod_id,
+                                                                    int32_t align, PackWs ws) {
+  __shared__ int32_t s_i32[kChunkThreads / 64 + 1];
+  __shared__ int64_t s_i64[kChunkThreads / 64 + 1];
   const int tid = threadIdx.x;
-  const int64_t b = blockIdx.x;
+  const int64_t c = blockIdx.x;
+  const int64_t b = c / n_ch;
+  const int32_t s0 = static_cast<int32_t>(c % n_ch) * kChunk + tid * kPer;
   const int64_t* row = tokens + b * seq;
-  int32_t* ends = ws.ends + b * seq;
 
-  if (tid == 0) s_valid = 0;
-  __syncthreads();
-  int last = 0;
-  for (int32_t s = tid; s < seq; s += kPackThreads)
-    if (row[s] != pad_id) last = max(last, s + 1);
-  if (last) atomicMax(&s_valid, last);
-  __syncthreads();
-  const int32_t valid_end = s_valid;
-
-  int32_t cnt = 0;
-  for (int32_t base = 0; base < valid_end; base += kPackThreads) {
-    const int32_t s = base + tid;
-    const bool eod = s < valid_end && row[s] == eod_id;
-    int sum;
-    const int off = block_exclusive_scan<kPackThreads, int>(eod ? 1 : 0, s_wave, &sum);
-    if (eod) ends[cnt + off] = s + 1;
-    cnt += sum;
+  int32_t lnp = 0, ne = 0, fe = INT32_MAX, le = 0;
+  bool eod[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int32_t s = s0 + i;
+    const int64_t v = s < seq ? row[s] : pad_id;
+    eod[i] = s < seq && v == eod_id;
+    if (v != pad_id) lnp = s + 1;
+    if (eod[i]) {
+      ++ne;
+      fe = min(fe, s + 1);
+      le = s + 1;
+    }
   }
-  __threadfence();
-  __syncthreads();
+  // the EOD before this thread's first one, inside the chunk (0: none)
+  int32_t le_all;
+  const int32_t prev = block_exclusive_max<kChunkThreads, int32_t>(le, 0, s_i32, &le_all);
+  int64_t ps = 0;  // padded lengths of documents with both ends in the chunk
+  int32_t last = prev;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (eod[i]) {
+      if (last > 0) ps += padded_len(s0 + i + 1 - last, align);
+      last = s0 + i + 1;
+    }
+  }
+  int32_t lnp_all, ne_all, neg_fe_all;
+  block_exclusive_max<kChunkThreads, int32_t>(lnp, 0, s_i32, &lnp_all);
+  block_exclusive_max<kChunkThreads, int32_t>(-fe, -INT32_MAX, s_i32, &neg_fe_all);
+  block_exclusive_scan<kChunkThreads, int32_t>(ne, s_i32, &ne_all);
+  int64_t ps_all;
+  block_exclusive_scan<kChunkThreads, int64_t>(ps, s_i64, &ps_all);
   if (tid == 0) {
-    const int32_t last_end = cnt ? ends[cnt - 1] : 0;
-    if (valid_end > last_end) ends[cnt++] = valid_end;  // the document after the last EOD
-    s_cnt = cnt;
-  }
-  __threadfence();
-  __syncthreads();
-  cnt = s_cnt;
-
-  int64_t padded = 0;
-  for (int32_t k = tid; k < cnt; k += kPackThreads) {
-    const int32_t len = ends[k] - (k ? ends[k - 1] : 0);
-    padded += len + (align - len % align) % align;
-  }
-  int64_t row_padded;
-  block_exclusive_scan<kPackThreads, int64_t>(padded, s_wave64, &row_padded);
-  if (tid == 0) {
-    ws.row_valid[b] = valid_end;
-    ws.row_docs[b] = cnt;
-    ws.row_padded[b] = row_padded;
+    ws.ch_lnp[c] = lnp_all;
+    ws.ch_ne[c] = ne_all;
+    ws.ch_fe[c] = ne_all ? -neg_fe_all : 0;
+    ws.ch_le[c] = le_all;
+    ws.ch_ps[c] = ps_all;
   }
 }
 
-// Prefix sums over rows, the budget checks and the boundary tails.
-__global__ __launch_bounds__(kPackThreads) void pack_meta_kernel(int32_t batch, int32_t max_docs, int32_t capacity,
+// Scan pass: one workgroup over all chunks in batch order.  Row boundaries
+// are handled without segmented scans: a position p of row b is keyed
+// b * (seq + 1) + p, so a running maximum never carries a value from an
+// earlier row past the row's own base key.
+__global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int64_t n_total, int32_t seq, int32_t n_ch,
+                                                                 int32_t align, int32_t max_docs, int32_t capacity,
                                                                  PackWs ws, int32_t* __restrict__ cu_real,
                                                                  int32_t* __restrict__ cu_pad,
                                                                  int32_t* __restrict__ status) {
-  __shared__ int64_t s_wave[kPackWaves + 1];
+  __shared__ int64_t s_wave[kScanThreads / 64 + 1];
   const int tid = threadIdx.x;
-  int64_t docs = 0, real = 0, padded = 0;
-  for (int32_t base = 0; base < batch; base += kPackThreads) {
-    const int32_t b = base + tid;
-    const bool in = b < batch;
-    int64_t sd, sr, sp;
-    const int64_t od = block_exclusive_scan<kPackThreads, int64_t>(in ? ws.row_docs[b] : 0, s_wave, &sd);
-    const int64_t orl = block_exclusive_scan<kPackThreads, int64_t>(in ? ws.row_valid[b] : 0, s_wave, &sr);
-    const int64_t op = block_exclusive_scan<kPackThreads, int64_t>(in ? ws.row_padded[b] : 0, s_wave, &sp);
-    if (in) {
-      ws.row_doc_off[b] = docs + od;
-      ws.row_real_off[b] = real + orl;
-      ws.row_pack_off[b] = padded + op;
+  const int64_t stride = static_cast<int64_t>(seq) + 1;
+  int64_t carry_eod = 0, carry_np = 0;         // running maxima of the keyed positions
+  int64_t carry_d = 0, carry_p = 0, carry_r = 0;  // running sums: documents, padded, real
+  for (int64_t base = 0; base < n_total; base += kScanThreads) {
+    const int64_t c = base + tid;
+    const bool in = c < n_total;
+    const int64_t b = in ? c / n_ch : 0;
+    const bool row_last = in && c % n_ch == n_ch - 1;
+    const int32_t ne = in ? ws.ch_ne[c] : 0;
+    const int64_t key0 = b * stride;
+    const int64_t k_eod = in ? key0 + (ne ? ws.ch_le[c] : 0) : 0;
+    const int64_t k_np = in ? key0 + ws.ch_lnp[c] : 0;
+    int64_t tot;
+    int64_t ex_eod = block_exclusive_max<kScanThreads, int64_t>(k_eod, 0, s_wave, &tot);
+    ex_eod = max(ex_eod, carry_eod);
+    carry_eod = max(carry_eod, tot);
+    int64_t ex_np = block_exclusive_max<kScanThreads, int64_t>(k_np, 0, s_wave, &tot);
+    ex_np = max(ex_np, carry_np);
+    carry_np = max(carry_np, tot);
+
+    // end of the last document closed before this chunk (row coordinates)
+    const int32_t prev_end = static_cast<int32_t>(max(ex_eod, key0) - key0);
+    int64_t d = ne, p = 0, r = 0;
+    if (ne) p = padded_len(ws.ch_fe[c] - prev_end, align) + ws.ch_ps[c];
+    if (row_last) {
+      const int32_t valid_end = static_cast<int32_t>(max(max(ex_np, k_np), key0) - key0);
+      const int32_t last_eod = static_cast<int32_t>(max(max(ex_eod, k_eod), key0) - key0);
+      if (valid_end > last_eod) {  // the document after the row's last EOD
+        d += 1;
+        p += padded_len(valid_end - last_eod, align);
+      }
+      r = valid_end;
+      ws.row_valid[b] = valid_end;
     }
-    docs += sd;
-    real += sr;
-    padded += sp;
+    int64_t td, tp, tr;
+    const int64_t ex_d = block_exclusive_scan<kScanThreads, int64_t>(d, s_wave, &td) + carry_d;
+    const int64_t ex_p = block_exclusive_scan<kScanThreads, int64_t>(p, s_wave, &tp) + carry_p;
+    const int64_t ex_r = block_exclusive_scan<kScanThreads, int64_t>(r, s_wave, &tr) + carry_r;
+    if (in) {
+      ws.ch_prev[c] = prev_end;
+      ws.ch_doc_base[c] = ex_d;
+      ws.ch_pack_base[c] = ex_p;
+      if (row_last) ws.row_real_off[b] = ex_r;  // real tokens of the earlier rows
+    }
+    carry_d += td;
+    carry_p += tp;
+    carry_r += tr;
   }
+  const int64_t docs = carry_d, padded = carry_p, real = carry_r;
   const int32_t code = docs > max_docs ? THD_ERR_PACK_DOCS : (padded > capacity ? THD_ERR_PACK_CAPACITY : THD_OK);
   if (tid == 0) {
     ws.hdr[0] = code;
@@ -118,94 +171,146 @@ __global__ __launch_bounds__(kPackThreads) void pack_meta_kernel(int32_t batch, 
     cu_pad[0] = 0;
   }
   // trailing pad slot (ends at the budget, no real tokens) and empty slots
-  for (int64_t k = docs + 1 + tid; k <= static_cast<int64_t>(max_docs) + 1; k += kPackThreads) {
+  for (int64_t k = docs + 1 + tid; k <= static_cast<int64_t>(max_docs) + 1; k += kScanThreads) {
     cu_real[k] = static_cast<int32_t>(real);
     cu_pad[k] = capacity;
   }
 }
 
-// Per row: the documents' boundaries, their tokens and their pads; all
-// workgroups together fill the trailing pad slot.
-__global__ __launch_bounds__(kPackThreads) void pack_write_kernel(const int64_t* __restrict__ tokens, int32_t batch,
-                                                                  int32_t seq, int32_t align, int64_t pad_value,
-                                                                  int32_t capacity, PackWs ws,
-                                                                  int64_t* __restrict__ packed,
-                                                                  int32_t* __restrict__ cu_real,
-                                                                  int32_t* __restrict__ cu_pad) {
-  __shared__ int64_t s_wave[kPackWaves + 1];
+struct PadRun {
+  int64_t start;  // packed position of the run's first pad
+  int64_t first;  // index of that pad among the chunk's pads
+};
+
+// Write pass: one workgroup per chunk, then every workgroup helps fill the
+// budget's tail.
+__global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t* __restrict__ tokens, int32_t seq,
+                                                                   int32_t n_ch, int64_t n_chunks, int64_t eod_id,
+                                                                   int32_t align, int64_t pad_value,
+                                                                   int32_t capacity, int32_t max_docs, PackWs ws,
+                                                                   int64_t* __restrict__ packed,
+                                                                   int32_t* __restrict__ cu_real,
+                                                                   int32_t* __restrict__ cu_pad) {
+  __shared__ int32_t s_i32[kChunkThreads / 64 + 1];
+  __shared__ int64_t s_i64[kChunkThreads / 64 + 1];
+  __shared__ PadRun s_pads[kChunk];
   if (ws.hdr[0] != THD_OK) return;  // over budget: nothing is written
   const int tid = threadIdx.x;
-  const int64_t b = blockIdx.x;
-  if (b < batch) {
-    const int64_t* row = tokens + b * seq;
-    const int32_t* ends = ws.ends + b * seq;
-    const int32_t cnt = ws.row_docs[b];
+  const int64_t c = blockIdx.x;
+  if (c < n_chunks) {
+    const int64_t b = c / n_ch;
     const int32_t valid_end = ws.row_valid[b];
-    const int64_t doc_off = ws.row_doc_off[b];
-    const int64_t real_off = ws.row_real_off[b];
-    const int64_t pack_off = ws.row_pack_off[b];
+    const int32_t s0 = static_cast<int32_t>(c % n_ch) * kChunk + tid * kPer;
+    const int64_t* row = tokens + b * seq;
+    if (static_cast<int32_t>(c % n_ch) * kChunk < valid_end) {  // uniform per workgroup
+      int64_t v[kPer];
+      bool end[kPer];
+      int32_t le = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int32_t s = s0 + i;
+        v[i] = s < valid_end ? row[s] : 0;
+        end[i] = s < valid_end && (v[i] == eod_id || s + 1 == valid_end);
+        if (end[i]) le = s + 1;
+      }
+      int32_t unused;
+      const int32_t start0 = max(block_exclusive_max<kChunkThreads, int32_t>(le, 0, s_i32, &unused), ws.ch_prev[c]);
+      int64_t plen_sum = 0, pad_sum = 0;
+      int32_t n_end = 0;
+      int32_t st = start0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (end[i]) {
+          const int64_t len = s0 + i + 1 - st;
+          const int64_t pl = padded_len(len, align);
+          plen_sum += pl;
+          pad_sum += pl - len;
+          ++n_end;
+          st = s0 + i + 1;
+        }
+      }
+      int64_t plen_total, pad_total;
+      int32_t end_total;
+      const int64_t pl_off = block_exclusive_scan<kChunkThreads, int64_t>(plen_sum, s_i64, &plen_total);
+      const int64_t pad_off = block_exclusive_scan<kChunkThreads, int64_t>(pad_sum, s_i64, &pad_total);
+      const int32_t end_off = block_exclusive_scan<kChunkThreads, int32_t>(n_end, s_i32, &end_total);
 
-    int64_t carry = pack_off;
-    for (int32_t base = 0; base < cnt; base += kPackThreads) {
-      const int32_t k = base + tid;
-      int64_t plen = 0;
-      if (k < cnt) {
-        const int32_t len = ends[k] - (k ? ends[k - 1] : 0);
-        plen = len + (align - len % align) % align;
+      const int64_t real_off = ws.row_real_off[b];
+      int64_t pos = ws.ch_pack_base[c] + pl_off;  // packed start of the current document
+      int64_t k = ws.ch_doc_base[c] + end_off;    // its index
+      int64_t pads_seen = pad_off;
+      int32_t slot = end_off;
+      st = start0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int32_t s = s0 + i;
+        // the scans keep every position inside the budget and every document
+        // inside the slots once the budget checks passed; the guards only
+        // make that independent of the workspace's contents
+        if (s < valid_end && pos + (s - st) < capacity) packed[pos + (s - st)] = v[i];
+        if (end[i]) {
+          const int64_t len = s + 1 - st;
+          const int64_t pl = padded_len(len, align);
+          if (k < max_docs) {
+            cu_real[k + 1] = static_cast<int32_t>(real_off + s + 1);
+            cu_pad[k + 1] = static_cast<int32_t>(pos + pl);
+          }
+          s_pads[slot] = PadRun{pos + len, pads_seen};
+          pads_seen += pl - len;
+          ++slot;
+          ++k;
+          pos += pl;
+          st = s + 1;
+        }
       }
-      int64_t sum;
-      const int64_t off = block_exclusive_scan<kPackThreads, int64_t>(plen, s_wave, &sum);
-      if (k < cnt) {
-        cu_pad[doc_off + k + 1] = static_cast<int32_t>(carry + off + plen);
-        cu_real[doc_off + k + 1] = static_cast<int32_t>(real_off + ends[k]);
+      __syncthreads();
+      // the chunk's pads, spread over every thread: pad q belongs to the last
+      // document end whose first pad index is <= q
+      for (int64_t q = tid; q < pad_total; q += kChunkThreads) {
+        int32_t lo = 0, hi = end_total;
+        while (hi - lo > 1) {
+          const int32_t mid = (lo + hi) >> 1;
+          if (s_pads[mid].first <= q) lo = mid;
+          else hi = mid;
+        }
+        const int64_t at = s_pads[lo].start + (q - s_pads[lo].first);
+        if (at < capacity) packed[at] = pad_value;
       }
-      carry += sum;
-    }
-    __threadfence();
-    __syncthreads();  // this row's boundaries are read back below
-
-    for (int32_t s = tid; s < valid_end; s += kPackThreads) {
-      int32_t lo = 0, hi = cnt - 1;  // document k: the first with ends[k] > s
-      while (lo < hi) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (ends[mid] > s) hi = mid;
-        else lo = mid + 1;
-      }
-      const int32_t start = lo ? ends[lo - 1] : 0;
-      const int64_t base_pos = lo ? static_cast<int64_t>(cu_pad[doc_off + lo]) : pack_off;
-      packed[base_pos + (s - start)] = row[s];
-    }
-    for (int32_t k = tid; k < cnt; k += kPackThreads) {
-      const int32_t len = ends[k] - (k ? ends[k - 1] : 0);
-      const int64_t begin = (k ? static_cast<int64_t>(cu_pad[doc_off + k]) : pack_off) + len;
-      const int64_t end = cu_pad[doc_off + k + 1];
-      for (int64_t p = begin; p < end; ++p) packed[p] = pad_value;
     }
   }
   const int64_t used = ws.hdr[2];
-  for (int64_t i = used + static_cast<int64_t>(blockIdx.x) * kPackThreads + tid; i < capacity;
-       i += static_cast<int64_t>(gridDim.x) * kPackThreads)
+  for (int64_t i = used + static_cast<int64_t>(blockIdx.x) * kChunkThreads + tid; i < capacity;
+       i += static_cast<int64_t>(gridDim.x) * kChunkThreads)
     packed[i] = pad_value;
 }
 
 }  // namespace
 
+int64_t pack_chunks(int32_t batch, int32_t seq) {
+  const int64_t n_ch = (static_cast<int64_t>(seq) + kChunk - 1) / kChunk;
+  return static_cast<int64_t>(batch) * n_ch;
+}
+
 hipError_t launch_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id,
                        int32_t align, int32_t capacity, int32_t max_docs, int64_t pad_value, const PackWs& ws,
                        int64_t* packed, int32_t* cu_real, int32_t* cu_pad, int32_t* status, hipStream_t stream) {
-  if (batch > 0) {
-    hipLaunchKernelGGL(pack_rows_kernel, dim3(batch), dim3(kPackThreads), 0, stream, tokens, seq, pad_id, eod_id,
-                       align, ws);
+  const int32_t n_ch = static_cast<int32_t>((static_cast<int64_t>(seq) + kChunk - 1) / kChunk);
+  const int64_t n_chunks = pack_chunks(batch, seq);
+  if (n_chunks > INT32_MAX) return hipErrorInvalidValue;
+  if (n_chunks > 0) {
+    hipLaunchKernelGGL(pack_chunks_kernel, dim3(static_cast<unsigned>(n_chunks)), dim3(kChunkThreads), 0, stream,
+                       tokens, seq, n_ch, pad_id, eod_id, align, ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pack_meta_kernel, dim3(1), dim3(kPackThreads), 0, stream, batch, max_docs, capacity, ws, cu_real,
-                     cu_pad, status);
+  hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, n_chunks, seq, n_ch > 0 ? n_ch : 1, align,
+                     max_docs, capacity, ws, cu_real, cu_pad, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int32_t grid = batch > 0 ? batch : 1;
-  hipLaunchKernelGGL(pack_write_kernel, dim3(grid), dim3(kPackThreads), 0, stream, tokens, batch, seq, align,
-                     pad_value, capacity, ws, packed, cu_real, cu_pad);
+  const int64_t grid = n_chunks > 0 ? n_chunks : 1;
+  hipLaunchKernelGGL(pack_write_kernel, dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), 0, stream, tokens,
+                     seq, n_ch > 0 ? n_ch : 1, n_chunks, eod_id, align, pad_value, capacity, max_docs, ws, packed,
+                     cu_real, cu_pad);
   return hipGetLastError();
 }
 

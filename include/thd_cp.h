@@ -74,6 +74,7 @@ extern "C" {
 #define THD_MAX_CP        1024
 #define THD_MAX_SHIFT     8
 #define THD_MAX_BATCH     16
+#define THD_PACK_MAX_SEQ  2147479552   /* 2^31 - 4096 tokens per packed row */
 
 typedef struct thd_route thd_route;   /* opaque; owns one device workspace */
 
@@ -206,7 +207,8 @@ int thd_roll_labels_zigzag(const thd_route* route, const int64_t* ids, const int
 
 /*
  * thd_pack_workspace_bytes -- device workspace thd_pack needs for a
- * [batch, seq] token matrix (host-only arithmetic; -1 for negative sizes).
+ * [batch, seq] token matrix (host-only arithmetic; -1 for negative sizes or
+ * seq > THD_PACK_MAX_SEQ).  About 40 bytes per 1024-token chunk of a row.
  */
 int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq);
 
@@ -237,8 +239,9 @@ int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq);
  * status:    device int32 or NULL: THD_OK, THD_ERR_PACK_DOCS or
  *            THD_ERR_PACK_CAPACITY; on an error nothing but status is written.
  *
- * Host errors: THD_ERR_ARG (negative sizes, align < 1, capacity not a multiple
- * of align, pad_id == eod_id, null pointers, workspace too small),
+ * Host errors: THD_ERR_ARG (negative sizes, seq > THD_PACK_MAX_SEQ, align < 1,
+ * capacity not a multiple of align, pad_id == eod_id, null pointers,
+ * workspace too small),
  * THD_ERR_ALIAS (outputs overlapping each other, the tokens or the workspace).
  * Three kernel launches.
  */

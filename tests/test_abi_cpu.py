@@ -97,6 +97,8 @@ def test_host_rejections_without_device_work(pkg):
     assert pack(eod=0) == pkg.THD_ERR_ARG
     assert pack(ws_bytes=ws - 1) == pkg.THD_ERR_ARG
     assert pack(batch=-1) == pkg.THD_ERR_ARG
+    assert pack(seq=pkg.THD_PACK_MAX_SEQ + 1) == pkg.THD_ERR_ARG
+    assert lib.thd_pack_workspace_bytes(1, pkg.THD_PACK_MAX_SEQ + 1) == -1
     assert pack(cu=(1 << 31) + 8) == pkg.THD_ERR_ALIAS
     assert pack(packed=(1 << 20) + 64) == pkg.THD_ERR_ALIAS
     # plain copy: negative size, null pointers, overlap; zero bytes launches nothing

@@ -51,7 +51,30 @@ CASES = [
     (4, 3, 2500, 0.0, 50, 0.0, 64, 128, 3),        # no EOD at all: one document per non-empty row
     (5, 2, 3000, 0.3, 10, 0.0, 4, 0, 0),           # EOD-dense: many one- and two-token documents
     (6, 1200, 17, 0.1, None, 0.1, 8, 1000, 10),    # many short rows
+    (7, 2, 3072, 0.001, 1024, 0.0, 512, 3, 2),      # rows of whole 1024-token chunks, wide alignment
+    (8, 3, 2048, 0.0, 1, 0.0, 3, 5, 1),             # one document per row crossing chunks, odd alignment
 ]
+
+
+def test_pack_chunk_boundaries(thd):
+    # EODs and valid ends on and next to the 1024-token chunk edges, where
+    # a document's start and end fall in different chunks.
+    import torch
+    seq = 4096
+    rows = np.full((6, seq), 5, dtype=np.int64)
+    for r, (eods, valid_end) in enumerate([([1023], 2048), ([1024], 1025), ([1022, 1023, 1024, 2047], 4096),
+                                           ([], 1024), ([0, 4095], 4096), ([3071], 3072)]):
+        rows[r, valid_end:] = PAD
+        rows[r, eods] = EOD
+    align, max_docs = 8, 20
+    capacity = 8 * 4096 + 64
+    want = O.pack_batch(rows, PAD, EOD, align, capacity, max_docs, -3)
+    packed, cu_real, cu_pad, status = thd.pack(dev_i64(rows), PAD, EOD, align, capacity, max_docs, -3)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(packed.cpu().numpy(), want[0])
+    assert np.array_equal(cu_real.cpu().numpy(), want[1])
+    assert np.array_equal(cu_pad.cpu().numpy(), want[2])
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"seed{c[0]}" for c in CASES])
