@@ -238,6 +238,7 @@ def oracle_baseline(w, layers, budget_s):
         "sample": f"{steps} full step(s) of the {w.name} workload ({layers} layer(s)), {el:.1f} s; "
                   f"single-threaded NumPy on 1 of {os.cpu_count()} host threads ({cpu_model()})",
         "ms_per_step": round(el / steps * 1e3, 1),
+        "step_tokens_per_s": round(w.total * steps / el),
     }
 
 
@@ -343,7 +344,7 @@ def main():
     # route build: host enqueue time of the build call alone (device time from the events above)
     torch.cuda.synchronize()
     enq = []
-    for _ in range(50):
+    for _ in range(100):
         t0 = time.perf_counter()
         thd.thd_build_route(h, cu, n_slots, cp, total, s_handle)
         enq.append(time.perf_counter() - t0)

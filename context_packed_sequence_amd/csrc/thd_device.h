@@ -40,43 +40,58 @@ __device__ T block_exclusive_scan(T v, T* s_wave, T* total) {
   return excl;
 }
 
-// Exclusive prefix maximum over a workgroup, same contract as
-// block_exclusive_scan: thread i gets the maximum of v over threads < i
-// (`lowest` for thread 0) and *total the maximum over all threads.
-template <int kThreads, typename T>
-__device__ T block_exclusive_max(T v, T lowest, T* s_wave, T* total) {
+// K independent exclusive scans over a workgroup in one pass (one set of
+// barriers): sums when kMax is false, maxima when it is true, with
+// `identity` as the value before thread 0.  excl[k] is thread i's result,
+// total[k] the workgroup's.  s is LDS scratch of K * (kThreads / 64 + 1).
+template <int kThreads, int K, bool kMax>
+__device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, int64_t* s, int64_t (&excl)[K],
+                                      int64_t (&total)[K]) {
   constexpr int kWaves = kThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  T x = v;  // inclusive maximum inside the wave
+  int64_t x[K], ex[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) x[k] = v[k];
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(x, o, 64);
-    if (lane >= o) x = x > y ? x : y;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t y = __shfl_up(x[k], o, 64);
+      if (lane >= o) x[k] = kMax ? (x[k] > y ? x[k] : y) : x[k] + y;
+    }
   }
-  T ex = __shfl_up(x, 1, 64);  // exclusive maximum inside the wave
-  if (lane == 0) ex = lowest;
-  if (lane == 63) s_wave[wave] = x;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    ex[k] = __shfl_up(x[k], 1, 64);
+    if (lane == 0) ex[k] = identity;
+    if (lane == 63) s[k * (kWaves + 1) + wave] = x[k];
+  }
   __syncthreads();
   if (wave == 0) {
-    const T w = lane < kWaves ? s_wave[lane] : lowest;
-    T xs = w;
 #pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const T y = __shfl_up(xs, o, 64);
-      if (lane >= o) xs = xs > y ? xs : y;
+    for (int k = 0; k < K; ++k) {
+      const int64_t w = lane < kWaves ? s[k * (kWaves + 1) + lane] : identity;
+      int64_t xs = w;
+#pragma unroll
+      for (int o = 1; o < kWaves; o <<= 1) {
+        const int64_t y = __shfl_up(xs, o, 64);
+        if (lane >= o) xs = kMax ? (xs > y ? xs : y) : xs + y;
+      }
+      int64_t prev = __shfl_up(xs, 1, 64);
+      if (lane == 0) prev = identity;
+      if (lane < kWaves) s[k * (kWaves + 1) + lane] = prev;
+      if (lane == kWaves - 1) s[k * (kWaves + 1) + kWaves] = xs;
     }
-    T prev = __shfl_up(xs, 1, 64);
-    if (lane == 0) prev = lowest;
-    if (lane < kWaves) s_wave[lane] = prev;
-    if (lane == kWaves - 1) s_wave[kWaves] = xs;
   }
   __syncthreads();
-  const T before = s_wave[wave];
-  const T excl = before > ex ? before : ex;
-  *total = s_wave[kWaves];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t before = s[k * (kWaves + 1) + wave];
+    excl[k] = kMax ? (before > ex[k] ? before : ex[k]) : before + ex[k];
+    total[k] = s[k * (kWaves + 1) + kWaves];
+  }
   __syncthreads();
-  return excl;
 }
 
 }  // namespace thdcp

@@ -41,21 +41,22 @@ constexpr int kChunkThreads = 256;
 constexpr int kPer = kChunk / kChunkThreads;  // consecutive tokens per thread
 constexpr int kScanThreads = 1024;
 
-__device__ __forceinline__ int64_t padded_len(int64_t len, int32_t align) {
-  return len + (align - len % align) % align;
+// Length of a document of `len` tokens once padded to a multiple of align.
+__device__ __forceinline__ int64_t padded_len(int32_t len, int32_t align) {
+  const int32_t r = len % align;
+  return static_cast<int64_t>(len) + (r ? align - r : 0);
 }
 
 // Chunk pass.
 __global__ __launch_bounds__(kChunkThreads) void pack_chunks_kernel(const int64_t* __restrict__ tokens, int32_t seq,
                                                                     int32_t n_ch, int64_t pad_id, int64_t eod_id,
                                                                     int32_t align, PackWs ws) {
-  __shared__ int32_t s_i32[kChunkThreads / 64 + 1];
-  __shared__ int64_t s_i64[kChunkThreads / 64 + 1];
+  __shared__ int64_t s_scan[3 * (kChunkThreads / 64 + 1)];
   const int tid = threadIdx.x;
-  const int64_t c = blockIdx.x;
-  const int64_t b = c / n_ch;
-  const int32_t s0 = static_cast<int32_t>(c % n_ch) * kChunk + tid * kPer;
-  const int64_t* row = tokens + b * seq;
+  const int32_t c = blockIdx.x;
+  const int32_t b = c / n_ch;
+  const int32_t s0 = (c - b * n_ch) * kChunk + tid * kPer;
+  const int64_t* row = tokens + static_cast<int64_t>(b) * seq;
 
   int32_t lnp = 0, ne = 0, fe = INT32_MAX, le = 0;
   bool eod[kPer];
@@ -71,11 +72,13 @@ __global__ __launch_bounds__(kChunkThreads) void pack_chunks_kernel(const int64_
       le = s + 1;
     }
   }
-  // the EOD before this thread's first one, inside the chunk (0: none)
-  int32_t le_all;
-  const int32_t prev = block_exclusive_max<kChunkThreads, int32_t>(le, 0, s_i32, &le_all);
+  // maxima: the last EOD before this thread inside the chunk (0: none), and
+  // the chunk's last non-PAD and (negated) first EOD
+  const int64_t mv[3] = {le, lnp, -static_cast<int64_t>(fe)};
+  int64_t mx[3], mt[3];
+  block_exclusive_multi<kChunkThreads, 3, true>(mv, -static_cast<int64_t>(INT32_MAX), s_scan, mx, mt);
   int64_t ps = 0;  // padded lengths of documents with both ends in the chunk
-  int32_t last = prev;
+  int32_t last = static_cast<int32_t>(max(mx[0], int64_t(0)));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (eod[i]) {
@@ -83,18 +86,15 @@ __global__ __launch_bounds__(kChunkThreads) void pack_chunks_kernel(const int64_
       last = s0 + i + 1;
     }
   }
-  int32_t lnp_all, ne_all, neg_fe_all;
-  block_exclusive_max<kChunkThreads, int32_t>(lnp, 0, s_i32, &lnp_all);
-  block_exclusive_max<kChunkThreads, int32_t>(-fe, -INT32_MAX, s_i32, &neg_fe_all);
-  block_exclusive_scan<kChunkThreads, int32_t>(ne, s_i32, &ne_all);
-  int64_t ps_all;
-  block_exclusive_scan<kChunkThreads, int64_t>(ps, s_i64, &ps_all);
+  const int64_t sv[2] = {ne, ps};
+  int64_t sx[2], st[2];
+  block_exclusive_multi<kChunkThreads, 2, false>(sv, 0, s_scan, sx, st);
   if (tid == 0) {
-    ws.ch_lnp[c] = lnp_all;
-    ws.ch_ne[c] = ne_all;
-    ws.ch_fe[c] = ne_all ? -neg_fe_all : 0;
-    ws.ch_le[c] = le_all;
-    ws.ch_ps[c] = ps_all;
+    ws.ch_lnp[c] = static_cast<int32_t>(mt[1]);
+    ws.ch_ne[c] = static_cast<int32_t>(st[0]);
+    ws.ch_fe[c] = st[0] ? static_cast<int32_t>(-mt[2]) : 0;
+    ws.ch_le[c] = static_cast<int32_t>(mt[0]);
+    ws.ch_ps[c] = st[1];
   }
 }
 
@@ -102,40 +102,45 @@ __global__ __launch_bounds__(kChunkThreads) void pack_chunks_kernel(const int64_
 // are handled without segmented scans: a position p of row b is keyed
 // b * (seq + 1) + p, so a running maximum never carries a value from an
 // earlier row past the row's own base key.
-__global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int64_t n_total, int32_t seq, int32_t n_ch,
+__global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int32_t n_total, int32_t seq, int32_t n_ch,
                                                                  int32_t align, int32_t max_docs, int32_t capacity,
                                                                  PackWs ws, int32_t* __restrict__ cu_real,
                                                                  int32_t* __restrict__ cu_pad,
                                                                  int32_t* __restrict__ status) {
-  __shared__ int64_t s_wave[kScanThreads / 64 + 1];
+  __shared__ int64_t s_scan[3 * (kScanThreads / 64 + 1)];
   const int tid = threadIdx.x;
   const int64_t stride = static_cast<int64_t>(seq) + 1;
-  int64_t carry_eod = 0, carry_np = 0;         // running maxima of the keyed positions
+  int64_t carry_eod = 0, carry_np = 0;            // running maxima of the keyed positions
   int64_t carry_d = 0, carry_p = 0, carry_r = 0;  // running sums: documents, padded, real
-  for (int64_t base = 0; base < n_total; base += kScanThreads) {
-    const int64_t c = base + tid;
+  for (int32_t base = 0; base < n_total; base += kScanThreads) {
+    const int32_t c = base + tid;
     const bool in = c < n_total;
-    const int64_t b = in ? c / n_ch : 0;
-    const bool row_last = in && c % n_ch == n_ch - 1;
-    const int32_t ne = in ? ws.ch_ne[c] : 0;
+    const int32_t b = in ? c / n_ch : 0;
+    const bool row_last = in && c - b * n_ch == n_ch - 1;
+    int32_t ne = 0, le = 0, lnp = 0, fe = 0;
+    int64_t ps = 0;
+    if (in) {
+      ne = ws.ch_ne[c];
+      le = ws.ch_le[c];
+      lnp = ws.ch_lnp[c];
+      fe = ws.ch_fe[c];
+      ps = ws.ch_ps[c];
+    }
     const int64_t key0 = b * stride;
-    const int64_t k_eod = in ? key0 + (ne ? ws.ch_le[c] : 0) : 0;
-    const int64_t k_np = in ? key0 + ws.ch_lnp[c] : 0;
-    int64_t tot;
-    int64_t ex_eod = block_exclusive_max<kScanThreads, int64_t>(k_eod, 0, s_wave, &tot);
-    ex_eod = max(ex_eod, carry_eod);
-    carry_eod = max(carry_eod, tot);
-    int64_t ex_np = block_exclusive_max<kScanThreads, int64_t>(k_np, 0, s_wave, &tot);
-    ex_np = max(ex_np, carry_np);
-    carry_np = max(carry_np, tot);
+    const int64_t mv[2] = {in ? key0 + le : 0, in ? key0 + lnp : 0};
+    int64_t mx[2], mt[2];
+    block_exclusive_multi<kScanThreads, 2, true>(mv, 0, s_scan, mx, mt);
+    const int64_t ex_eod = max(mx[0], carry_eod), ex_np = max(mx[1], carry_np);
+    carry_eod = max(carry_eod, mt[0]);
+    carry_np = max(carry_np, mt[1]);
 
     // end of the last document closed before this chunk (row coordinates)
     const int32_t prev_end = static_cast<int32_t>(max(ex_eod, key0) - key0);
     int64_t d = ne, p = 0, r = 0;
-    if (ne) p = padded_len(ws.ch_fe[c] - prev_end, align) + ws.ch_ps[c];
+    if (ne) p = padded_len(fe - prev_end, align) + ps;
     if (row_last) {
-      const int32_t valid_end = static_cast<int32_t>(max(max(ex_np, k_np), key0) - key0);
-      const int32_t last_eod = static_cast<int32_t>(max(max(ex_eod, k_eod), key0) - key0);
+      const int32_t valid_end = static_cast<int32_t>(max(max(ex_np, mv[1]), key0) - key0);
+      const int32_t last_eod = static_cast<int32_t>(max(max(ex_eod, mv[0]), key0) - key0);
       if (valid_end > last_eod) {  // the document after the row's last EOD
         d += 1;
         p += padded_len(valid_end - last_eod, align);
@@ -143,19 +148,18 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int64_t n_total
       r = valid_end;
       ws.row_valid[b] = valid_end;
     }
-    int64_t td, tp, tr;
-    const int64_t ex_d = block_exclusive_scan<kScanThreads, int64_t>(d, s_wave, &td) + carry_d;
-    const int64_t ex_p = block_exclusive_scan<kScanThreads, int64_t>(p, s_wave, &tp) + carry_p;
-    const int64_t ex_r = block_exclusive_scan<kScanThreads, int64_t>(r, s_wave, &tr) + carry_r;
+    const int64_t sv[3] = {d, p, r};
+    int64_t sx[3], st[3];
+    block_exclusive_multi<kScanThreads, 3, false>(sv, 0, s_scan, sx, st);
     if (in) {
       ws.ch_prev[c] = prev_end;
-      ws.ch_doc_base[c] = ex_d;
-      ws.ch_pack_base[c] = ex_p;
-      if (row_last) ws.row_real_off[b] = ex_r;  // real tokens of the earlier rows
+      ws.ch_doc_base[c] = carry_d + sx[0];
+      ws.ch_pack_base[c] = carry_p + sx[1];
+      if (row_last) ws.row_real_off[b] = carry_r + sx[2];  // real tokens of the earlier rows
     }
-    carry_d += td;
-    carry_p += tp;
-    carry_r += tr;
+    carry_d += st[0];
+    carry_p += st[1];
+    carry_r += st[2];
   }
   const int64_t docs = carry_d, padded = carry_p, real = carry_r;
   const int32_t code = docs > max_docs ? THD_ERR_PACK_DOCS : (padded > capacity ? THD_ERR_PACK_CAPACITY : THD_OK);
@@ -185,24 +189,24 @@ struct PadRun {
 // Write pass: one workgroup per chunk, then every workgroup helps fill the
 // budget's tail.
 __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t* __restrict__ tokens, int32_t seq,
-                                                                   int32_t n_ch, int64_t n_chunks, int64_t eod_id,
+                                                                   int32_t n_ch, int32_t n_chunks, int64_t eod_id,
                                                                    int32_t align, int64_t pad_value,
                                                                    int32_t capacity, int32_t max_docs, PackWs ws,
                                                                    int64_t* __restrict__ packed,
                                                                    int32_t* __restrict__ cu_real,
                                                                    int32_t* __restrict__ cu_pad) {
-  __shared__ int32_t s_i32[kChunkThreads / 64 + 1];
-  __shared__ int64_t s_i64[kChunkThreads / 64 + 1];
+  __shared__ int64_t s_scan[3 * (kChunkThreads / 64 + 1)];
   __shared__ PadRun s_pads[kChunk];
   if (ws.hdr[0] != THD_OK) return;  // over budget: nothing is written
   const int tid = threadIdx.x;
-  const int64_t c = blockIdx.x;
+  const int32_t c = blockIdx.x;
   if (c < n_chunks) {
-    const int64_t b = c / n_ch;
+    const int32_t b = c / n_ch;
     const int32_t valid_end = ws.row_valid[b];
-    const int32_t s0 = static_cast<int32_t>(c % n_ch) * kChunk + tid * kPer;
-    const int64_t* row = tokens + b * seq;
-    if (static_cast<int32_t>(c % n_ch) * kChunk < valid_end) {  // uniform per workgroup
+    const int32_t chunk_start = (c - b * n_ch) * kChunk;
+    const int32_t s0 = chunk_start + tid * kPer;
+    const int64_t* row = tokens + static_cast<int64_t>(b) * seq;
+    if (chunk_start < valid_end) {  // uniform per workgroup
       int64_t v[kPer];
       bool end[kPer];
       int32_t le = 0;
@@ -213,15 +217,16 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
         end[i] = s < valid_end && (v[i] == eod_id || s + 1 == valid_end);
         if (end[i]) le = s + 1;
       }
-      int32_t unused;
-      const int32_t start0 = max(block_exclusive_max<kChunkThreads, int32_t>(le, 0, s_i32, &unused), ws.ch_prev[c]);
-      int64_t plen_sum = 0, pad_sum = 0;
-      int32_t n_end = 0;
+      const int64_t mv[1] = {le};
+      int64_t mx[1], mt[1];
+      block_exclusive_multi<kChunkThreads, 1, true>(mv, 0, s_scan, mx, mt);
+      const int32_t start0 = max(static_cast<int32_t>(mx[0]), ws.ch_prev[c]);
+      int64_t plen_sum = 0, pad_sum = 0, n_end = 0;
       int32_t st = start0;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         if (end[i]) {
-          const int64_t len = s0 + i + 1 - st;
+          const int32_t len = s0 + i + 1 - st;
           const int64_t pl = padded_len(len, align);
           plen_sum += pl;
           pad_sum += pl - len;
@@ -229,11 +234,13 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
           st = s0 + i + 1;
         }
       }
-      int64_t plen_total, pad_total;
-      int32_t end_total;
-      const int64_t pl_off = block_exclusive_scan<kChunkThreads, int64_t>(plen_sum, s_i64, &plen_total);
-      const int64_t pad_off = block_exclusive_scan<kChunkThreads, int64_t>(pad_sum, s_i64, &pad_total);
-      const int32_t end_off = block_exclusive_scan<kChunkThreads, int32_t>(n_end, s_i32, &end_total);
+      const int64_t sv[3] = {plen_sum, pad_sum, n_end};
+      int64_t sx[3], stot[3];
+      block_exclusive_multi<kChunkThreads, 3, false>(sv, 0, s_scan, sx, stot);
+      const int64_t pl_off = sx[0], pad_off = sx[1], pad_total = stot[1];
+      // a chunk holds at most kChunk document ends
+      const int32_t end_off = static_cast<int32_t>(sx[2]);
+      const int32_t end_total = static_cast<int32_t>(min(stot[2], static_cast<int64_t>(kChunk)));
 
       const int64_t real_off = ws.row_real_off[b];
       int64_t pos = ws.ch_pack_base[c] + pl_off;  // packed start of the current document
@@ -249,13 +256,13 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
         // make that independent of the workspace's contents
         if (s < valid_end && pos + (s - st) < capacity) packed[pos + (s - st)] = v[i];
         if (end[i]) {
-          const int64_t len = s + 1 - st;
+          const int32_t len = s + 1 - st;
           const int64_t pl = padded_len(len, align);
           if (k < max_docs) {
             cu_real[k + 1] = static_cast<int32_t>(real_off + s + 1);
             cu_pad[k + 1] = static_cast<int32_t>(pos + pl);
           }
-          s_pads[slot] = PadRun{pos + len, pads_seen};
+          if (slot < kChunk) s_pads[slot] = PadRun{pos + len, pads_seen};
           pads_seen += pl - len;
           ++slot;
           ++k;
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
       __syncthreads();
       // the chunk's pads, spread over every thread: pad q belongs to the last
       // document end whose first pad index is <= q
-      for (int64_t q = tid; q < pad_total; q += kChunkThreads) {
+      for (int64_t q = tid; end_total > 0 && q < pad_total; q += kChunkThreads) {
         int32_t lo = 0, hi = end_total;
         while (hi - lo > 1) {
           const int32_t mid = (lo + hi) >> 1;
@@ -303,14 +310,15 @@ hipError_t launch_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, n_chunks, seq, n_ch > 0 ? n_ch : 1, align,
-                     max_docs, capacity, ws, cu_real, cu_pad, status);
+  const int32_t n_ch_arg = n_ch > 0 ? n_ch : 1;
+  hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, static_cast<int32_t>(n_chunks), seq,
+                     n_ch_arg, align, max_docs, capacity, ws, cu_real, cu_pad, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t grid = n_chunks > 0 ? n_chunks : 1;
   hipLaunchKernelGGL(pack_write_kernel, dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), 0, stream, tokens,
-                     seq, n_ch > 0 ? n_ch : 1, n_chunks, eod_id, align, pad_value, capacity, max_docs, ws, packed,
-                     cu_real, cu_pad);
+                     seq, n_ch_arg, static_cast<int32_t>(n_chunks), eod_id, align, pad_value, capacity, max_docs, ws,
+                     packed, cu_real, cu_pad);
   return hipGetLastError();
 }
 
