@@ -80,16 +80,53 @@ __device__ __forceinline__ Cut cut_segment(const Segment& s, int32_t share) {
 // uses the route's global scratch and global atomics (same steps, slower).
 constexpr int kBuildLdsBytes = 60 * 1024;
 
-template <bool kLds>
+// Fused build: when the runs of both orders fit in LDS as well, every
+// workgroup of one launch builds the whole route in its own LDS (the work is
+// small at these sizes and identical in every workgroup), workgroup 0 writes
+// it out, and each workgroup then writes its share of the directory from its
+// LDS copy.  One launch instead of build + directory, and no workgroup ever
+// waits for another.
+constexpr int kFusedMaxSegments = 4096;
+constexpr int kDirPerFusedGroup = 1024;  // directory rows per workgroup and direction
+
+// Largest i in [lo, hi) with runs[i].out <= row, given runs[lo].out <= row.
+__device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, int32_t lo, int32_t hi, int32_t row) {
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (runs[mid].out <= row) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Directory entry of output row `row` from a run table of one order.
+__device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, int32_t n_runs, int32_t row,
+                                              int32_t total) {
+  const RunPair r = runs[k];
+  DirEntry e;
+  e.in = r.in + (row - r.out);
+  e.run_end = k + 1 < n_runs ? runs[k + 1].out : total;
+  e.run = k;
+  e.pad = 0;
+  return e;
+}
+
+template <bool kLds, bool kFused>
 __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
-                                                                    int32_t cp, int32_t total, RouteDev ws) {
-  extern __shared__ int32_t s_dyn[];  // kLds: docs[3 * n_slots], split[cp * cp]
+                                                                    int32_t cp, int32_t total, RouteDev ws,
+                                                                    int32_t lds_run_cap) {
+  // kLds: docs[3 * n_slots], split[cp * cp]; kFused adds, 8-byte aligned,
+  // runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
+  extern __shared__ int32_t s_dyn[];
   __shared__ int s_wave[kBuildWaves + 1];
   __shared__ int s_sev;
   const int tid = threadIdx.x;
+  const bool writer = !kFused || blockIdx.x == 0;  // the workgroup that writes the route out
   const int32_t cap = kLds ? n_slots : ws.docs_cap;
   int32_t* docs = kLds ? s_dyn : ws.docs;
   int32_t* split = kLds ? s_dyn + 3 * n_slots : ws.split;
+  RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + cp * cp + 1) & ~1));
+  RunPair* l_dst = l_src + lds_run_cap;
 
   if (tid == 0) s_sev = 0;
   for (int i = tid; i < cp * cp; i += kBuildThreads) {
@@ -130,7 +167,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   if constexpr (!kLds) __threadfence();  // global path: zeroed split and document list are complete
   __syncthreads();                       // publishes the document list to the whole workgroup
   if (s_sev) {
-    if (tid == 0) {
+    if (tid == 0 && writer) {
       ws.hdr[kHdrRunsSrc] = 0;
       ws.hdr[kHdrRunsDst] = 0;
       ws.hdr[kHdrDocs] = 0;
@@ -196,15 +233,23 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
         atomicAdd(&split[ss.rank * cp + cs.first_d + p], pend - ptok);
         if (p >= merge_s) {
           const int64_t slot = static_cast<int64_t>(n_src) + off_s + p - merge_s;
-          if (slot < ws.run_cap) ws.runs_src[slot] = RunPair{ss.src + (ptok - ss.tok), ptok};
-          else overflow = true;
+          const RunPair run{ss.src + (ptok - ss.tok), ptok};
+          if (slot >= ws.run_cap || (kFused && slot >= lds_run_cap)) overflow = true;
+          else {
+            if (writer) ws.runs_src[slot] = run;
+            if constexpr (kFused) l_src[slot] = run;
+          }
         }
       }
       for (int p = merge_t; p < ct.pieces; ++p) {
         const int32_t ptok = p == 0 ? st.tok : (ct.first_d + p) * share;
         const int64_t slot = static_cast<int64_t>(n_dst) + off_t + p - merge_t;
-        if (slot < ws.run_cap) ws.runs_dst[slot] = RunPair{ptok, st.src + (ptok - st.tok)};
-        else overflow = true;
+        const RunPair run{ptok, st.src + (ptok - st.tok)};
+        if (slot >= ws.run_cap || (kFused && slot >= lds_run_cap)) overflow = true;
+        else {
+          if (writer) ws.runs_dst[slot] = run;
+          if constexpr (kFused) l_dst[slot] = run;
+        }
       }
     }
     n_src += sum & 0xFFFF;
@@ -229,11 +274,12 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     if (row != share || col != share) bad = true;
   }
   if constexpr (kLds) {
-    for (int i = tid; i < cp * cp; i += kBuildThreads) ws.split[i] = split[i];
+    if (writer)
+      for (int i = tid; i < cp * cp; i += kBuildThreads) ws.split[i] = split[i];
   }
   if (bad) atomicMax(&s_sev, 1);
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0 && writer) {
     ws.hdr[kHdrRunsSrc] = n_src;
     ws.hdr[kHdrRunsDst] = n_dst;
     ws.hdr[kHdrDocs] = n_docs;
@@ -241,16 +287,18 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     ws.hdr[kHdrTotal] = total;
     ws.hdr[kHdrStatus] = s_sev ? THD_ERR_INTEGRITY : THD_OK;
   }
-}
-
-// Largest i in [lo, hi) with runs[i].out <= row, given runs[lo].out <= row.
-__device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, int32_t lo, int32_t hi, int32_t row) {
-  while (hi - lo > 1) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (runs[mid].out <= row) lo = mid;
-    else hi = mid;
+  if constexpr (kFused) {
+    // ---- 6. this workgroup's share of the directory, both directions ----
+    if (s_sev) return;  // a failed route is never read past its status
+    const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
+    const int32_t b0 = blockIdx.x * kDirPerFusedGroup;
+    const int32_t b1 = min(n_blocks, b0 + kDirPerFusedGroup);
+    for (int32_t b = b0 + tid; b < b1; b += kBuildThreads) {
+      const int32_t row = b << kDirShift;
+      ws.dir_dst[b] = dir_entry(l_dst, last_run_at_or_before(l_dst, 0, n_dst, row), n_dst, row, total);
+      ws.dir_src[b] = dir_entry(l_src, last_run_at_or_before(l_src, 0, n_src, row), n_src, row, total);
+    }
   }
-  return lo;
 }
 
 // The same search done by one wave: each round, 64 lanes probe 64 evenly
@@ -335,15 +383,30 @@ __global__ __launch_bounds__(kIndexThreads) void route_index_kernel(RouteDev ws,
 
 }  // namespace
 
+bool route_build_fused(int32_t n_slots, int32_t cp) {
+  const int64_t segments = 2LL * cp * n_slots;
+  const int64_t run_cap = segments + cp;
+  const int64_t lds = 4 * ((3LL * n_slots + static_cast<int64_t>(cp) * cp + 1) & ~1LL) + 16 * run_cap;
+  return segments <= kFusedMaxSegments && lds <= kBuildLdsBytes;
+}
+
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total, const RouteDev& ws,
                               hipStream_t stream) {
   const int64_t lds = 4 * (3 * static_cast<int64_t>(n_slots) + static_cast<int64_t>(cp) * cp);
-  if (lds <= kBuildLdsBytes)
-    hipLaunchKernelGGL(route_build_kernel<true>, dim3(1), dim3(kBuildThreads), static_cast<size_t>(lds), stream, cu,
-                       n_slots, cp, total, ws);
-  else
-    hipLaunchKernelGGL(route_build_kernel<false>, dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp, total,
-                       ws);
+  if (route_build_fused(n_slots, cp)) {
+    const int32_t run_cap = 2 * cp * n_slots + cp;
+    const int64_t lds_fused = 4 * ((3LL * n_slots + static_cast<int64_t>(cp) * cp + 1) & ~1LL) + 16LL * run_cap;
+    const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
+    const int32_t grid = n_blocks > 0 ? (n_blocks + kDirPerFusedGroup - 1) / kDirPerFusedGroup : 1;
+    hipLaunchKernelGGL((route_build_kernel<true, true>), dim3(grid), dim3(kBuildThreads),
+                       static_cast<size_t>(lds_fused), stream, cu, n_slots, cp, total, ws, run_cap);
+  } else if (lds <= kBuildLdsBytes) {
+    hipLaunchKernelGGL((route_build_kernel<true, false>), dim3(1), dim3(kBuildThreads), static_cast<size_t>(lds),
+                       stream, cu, n_slots, cp, total, ws, 0);
+  } else {
+    hipLaunchKernelGGL((route_build_kernel<false, false>), dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp,
+                       total, ws, 0);
+  }
   return hipGetLastError();
 }
 

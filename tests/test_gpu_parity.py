@@ -264,3 +264,27 @@ def test_plain_copy(thd, nbytes, offset):
     torch.cuda.synchronize()
     assert torch.equal(dst[offset:offset + nbytes], src[offset:offset + nbytes])
     assert (dst[:offset] == 7).all() and (dst[offset + nbytes:] == 7).all()
+
+
+@pytest.mark.parametrize("seed,cp,docs,max_chunk,n_empty,rb", [
+    (400, 4, 290, 2, 10, 8),      # ~2400 segments: the one-launch build writes the directory
+    (401, 16, 60, 3, 4, 4096),    # cp 16, many directory workgroups, 4 KiB rows
+    (402, 2, 700, 3, 20, 1),      # cp 2 near the fused limit, one-byte rows
+    (403, 4, 490, 2, 10, 8),      # ~4000 segments: too many runs for LDS, build + directory kernels
+    (404, 8, 60, 40, 3, 16),      # long chunks: few runs, two directory workgroups
+    (405, 4, 200, 100, 5, 8),     # mixed runs over five directory workgroups
+])
+def test_route_build_with_and_without_fused_directory(thd, seed, cp, docs, max_chunk, n_empty, rb):
+    # Batches on both sides of the one-launch build's limits (runs of both
+    # orders held in LDS); dense short runs make every directory entry count.
+    import torch
+    w = W.random_packed(seed, cp, docs, max_chunk, n_empty, row_shape=(rb,), row_dtype="uint8")
+    cu, total = w.cu_padded, w.total
+    say("fused directory", seed, cp, "slots", w.n_slots, "T", total, "rb", rb)
+    route = build(thd, cu, cp, total)
+    check_route_matches_oracle(route, cu, cp, total)
+    x = torch.from_numpy(w.rows_host()).cuda()
+    for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+        out = route.swap(x, d)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), O.swap_rows(w.rows_host(), cu, cp, total, direction)), direction
