@@ -60,14 +60,33 @@ Z2C = THD_ZIGZAG_TO_CONTIGUOUS
 C2Z = THD_CONTIGUOUS_TO_ZIGZAG
 
 
+def _need(t, name, dtype=None, numel=None, device=None):
+    """Shape/dtype checks the C ABI cannot make: it sees only pointers, so a
+    too-small or wrongly typed buffer would be read or written out of bounds."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 class Route:
     """A device-resident zigzag <-> contiguous route.
 
     ``Route(max_slots, max_cp, max_tokens)`` allocates the workspace once;
-    ``build(cu_seqlens_padded, cp_size)`` rebuilds it for a new micro-batch
-    without waiting for the GPU; ``swap(x, direction)`` moves the rows of
-    ``x`` ([T, ...], token dimension first) and returns a new tensor, or ``x``
-    itself when the route is the identity.
+    ``build(cu_seqlens_padded, cp_size, total_tokens)`` rebuilds it for a new
+    micro-batch without waiting for the GPU; ``swap(x, direction)`` moves the
+    rows of ``x`` ([T, ...], token dimension first) and returns a new tensor,
+    or ``x`` itself when the route is the identity.
     """
 
     def __init__(self, max_slots: int, max_cp: int, max_tokens: int):
@@ -91,19 +110,24 @@ class Route:
     def __exit__(self, *exc):
         self.close()
 
-    def build(self, cu_seqlens_padded, cp_size: int, total_tokens: int | None = None, stream=None) -> "Route":
+    def build(self, cu_seqlens_padded, cp_size: int, total_tokens: int, stream=None) -> "Route":
+        """total_tokens is passed in because the boundaries stay on the device."""
+        import torch
+        _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32)
         n_slots = int(cu_seqlens_padded.numel()) - 1
-        if total_tokens is None:
-            raise ValueError("total_tokens is required (the boundaries stay on the device)")
         thd_build_route(self.handle, cu_seqlens_padded, n_slots, cp_size, total_tokens, stream)
         self.total = int(total_tokens)
         return self
 
     def swap(self, x, direction: int, out=None, stream=None):
         import torch
+        if x.dim() == 0:
+            raise ValueError("x needs a token dimension")
+        _need(x, "x")
         if out is None:
             out = torch.empty_like(x, memory_format=torch.contiguous_format)
-        rows = x.shape[0] if x.dim() else 0
+        _need(out, "out", x.dtype, x.numel(), x.device)
+        rows = x.shape[0]
         row_bytes = x.element_size() * (x.numel() // rows if rows else 1)
         code = thd_swap(self.handle, direction, x, out, rows, max(row_bytes, 1), stream)
         return x if code == THD_IDENTITY else out
@@ -112,9 +136,19 @@ class Route:
         """Swap several tensors (same token count) in one launch; returns the
         outputs, or the inputs themselves when the route is the identity."""
         import torch
+        if not xs:
+            raise ValueError("swap_many needs at least one tensor")
+        rows = xs[0].shape[0]
+        for i, x in enumerate(xs):
+            if x.dim() == 0 or x.shape[0] != rows:
+                raise ValueError(f"tensor {i} does not have {rows} rows")
+            _need(x, f"xs[{i}]")
         if outs is None:
             outs = [torch.empty_like(x, memory_format=torch.contiguous_format) for x in xs]
-        rows = xs[0].shape[0]
+        if len(outs) != len(xs):
+            raise ValueError("outs and xs differ in length")
+        for i, (x, o) in enumerate(zip(xs, outs)):
+            _need(o, f"outs[{i}]", x.dtype, x.numel(), x.device)
         row_bytes = [max(1, x.element_size() * (x.numel() // rows if rows else 1)) for x in xs]
         code = thd_swap_batch(self.handle, direction, xs, outs, row_bytes, rows, stream)
         return list(xs) if code == THD_IDENTITY else outs
@@ -125,6 +159,7 @@ class Route:
         order: shifted [max_shift, T] int64, mask [max_shift + 1, T] uint8,
         status int32 [1]."""
         import torch
+        _check_roll_inputs(ids, cu_seqlens_padded, cu_seqlens)
         total = int(ids.numel())
         shifted = torch.empty((max_shift, total), dtype=torch.int64, device=ids.device)
         mask = torch.empty((max_shift + 1, total), dtype=torch.uint8, device=ids.device)
@@ -144,11 +179,20 @@ class Route:
         return thd_route_info(self.handle)
 
 
+def _check_roll_inputs(ids, cu_seqlens_padded, cu_seqlens):
+    import torch
+    _need(ids, "ids", torch.int64)
+    _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, device=ids.device)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens_padded.numel(), ids.device)
+
+
 def roll_labels(ids, cu_seqlens_padded, cu_seqlens=None, max_shift: int = 1, fill: int = 0, stream=None,
                 with_status: bool = True):
     """Shifted label streams [max_shift, T] (int64), masks [max_shift + 1, T]
     (uint8) and, if asked, a device status word (int32 [1])."""
     import torch
+    _check_roll_inputs(ids, cu_seqlens_padded, cu_seqlens)
     total = int(ids.numel())
     shifted = torch.empty((max_shift, total), dtype=torch.int64, device=ids.device)
     mask = torch.empty((max_shift + 1, total), dtype=torch.uint8, device=ids.device)
@@ -166,6 +210,9 @@ def pack(tokens, pad_id: int, eod_id: int, align: int, capacity: int, max_docs: 
     [max_docs + 2] int32, status int32 [1]); the route and the roll take
     n_slots = max_docs + 1 and total_tokens = capacity."""
     import torch
+    _need(tokens, "tokens", torch.int64)
+    if tokens.dim() > 2:
+        raise ValueError("tokens must be [batch, seq] or [seq]")
     batch, seq = (int(tokens.shape[0]), int(tokens.shape[1])) if tokens.dim() == 2 else (1, int(tokens.numel()))
     dev = tokens.device
     nbytes = thd_pack_workspace_bytes(batch, seq)

@@ -123,3 +123,20 @@ def test_package_and_oracle_share_no_code():
             if f.endswith(".py"):
                 src = open(os.path.join(d, f), encoding="utf-8").read()
                 assert not re.search(rf"^\s*(from|import)\s+{other}\b", src, flags=re.M), (d, f)
+
+
+def test_wrappers_reject_wrong_buffers_before_any_device_call(pkg):
+    # The C ABI sees bare pointers; the Python wrappers check dtypes and sizes
+    # first, so a wrongly typed or short buffer never reaches a kernel.
+    import torch
+    cu = torch.tensor([0, 4, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="ids must be torch.int64"):
+        pkg.roll_labels(torch.zeros(8, dtype=torch.int32), cu)
+    with pytest.raises(ValueError, match="cu_seqlens_padded must be torch.int32"):
+        pkg.roll_labels(torch.zeros(8, dtype=torch.int64), cu.long())
+    with pytest.raises(ValueError, match="cu_seqlens must have 3 elements"):
+        pkg.roll_labels(torch.zeros(8, dtype=torch.int64), cu, torch.tensor([0, 4], dtype=torch.int32))
+    with pytest.raises(ValueError, match="tokens must be torch.int64"):
+        pkg.pack(torch.zeros((2, 4), dtype=torch.int32), 0, 1, 4, 16, 4)
+    with pytest.raises(ValueError, match="must be contiguous"):
+        pkg.pack(torch.zeros((4, 2), dtype=torch.int64).t(), 0, 1, 4, 16, 4)

@@ -133,6 +133,18 @@ def test_host_side_errors(thd):
     out = route.swap(x, thd.Z2C)
     torch.cuda.synchronize()
     assert out.shape == x.shape
+    # the wrappers refuse output buffers that do not match the input before
+    # any launch (the C ABI would write rows x row_bytes bytes into them)
+    short = torch.zeros(31, 8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="elements"):
+        route.swap(x, thd.Z2C, out=short)
+    with pytest.raises(ValueError, match="must be torch.uint8"):
+        route.swap(x, thd.Z2C, out=torch.zeros(32, 8, dtype=torch.int16, device="cuda"))
+    with pytest.raises(ValueError, match="rows"):
+        route.swap_many([x, torch.zeros(16, 8, dtype=torch.uint8, device="cuda")], thd.Z2C)
+    with pytest.raises(ValueError, match="elements"):
+        route.swap_many([x], thd.Z2C, outs=[short])
+    assert (short == 0).all()
 
 
 def test_identity_routes(thd):
