@@ -39,8 +39,15 @@ struct DirEntry {
   int32_t in;       // input row that feeds output row 16*b
   int32_t run_end;  // first output row after the run that holds 16*b
   int32_t run;      // index of that run
-  int32_t pad;
+  uint32_t starts;  // bit i (1..15): a run starts at output row 16*b + i
 };
+
+// Index of the run that holds output row r, from r's directory entry: the
+// entry's run plus the runs that start inside the block at or before r.
+__host__ __device__ inline int32_t run_of_row(const DirEntry& e, int32_t r) {
+  const uint32_t upto = (2u << (r & (kDirBlock - 1))) - 1u;  // bits 0..(r mod 16)
+  return e.run + __builtin_popcount(e.starts & upto & ~1u);
+}
 
 // Device pointers into the route workspace.
 struct RouteDev {

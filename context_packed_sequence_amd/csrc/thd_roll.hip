@@ -31,9 +31,7 @@ constexpr int kRollLdsSlots = 4096;  // boundaries staged in LDS (dynamic, 8 B p
 __device__ __forceinline__ int32_t zigzag_row_of(const RollRoute& rt, int32_t n_runs, int32_t t) {
   const DirEntry e = rt.dir[t >> kDirShift];
   if (t < e.run_end) return e.in + (t & (kDirBlock - 1));
-  int32_t k = e.run + 1;
-  while (k + 1 < n_runs && rt.runs[k + 1].out <= t) ++k;
-  k = min(k, n_runs - 1);
+  const int32_t k = min(run_of_row(e, t), n_runs - 1);
   const RunPair r = rt.runs[k];
   return r.in + (t - r.out);
 }

@@ -99,7 +99,8 @@ __device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, in
   return lo;
 }
 
-// Directory entry of output row `row` from a run table of one order.
+// Directory entry of output row `row` (a multiple of kDirBlock) from a run
+// table of one order, given the run k that holds it.
 __device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, int32_t n_runs, int32_t row,
                                               int32_t total) {
   const RunPair r = runs[k];
@@ -107,7 +108,8 @@ __device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, in
   e.in = r.in + (row - r.out);
   e.run_end = k + 1 < n_runs ? runs[k + 1].out : total;
   e.run = k;
-  e.pad = 0;
+  e.starts = 0;
+  for (int32_t j = k + 1; j < n_runs && runs[j].out < row + kDirBlock; ++j) e.starts |= 1u << (runs[j].out - row);
   return e;
 }
 
@@ -348,7 +350,9 @@ __global__ __launch_bounds__(kIndexThreads) void route_index_kernel(RouteDev ws,
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
     const int32_t k_lo = s_k[d][0];
-    const int32_t cnt = min(s_k[d][1] + 2, n_runs[d]) - k_lo;  // window's runs plus the one after
+    // the window's runs plus the kDirBlock after it: every run that starts
+    // inside the window's last directory block, and the one after that
+    const int32_t cnt = min(s_k[d][1] + kDirBlock + 1, n_runs[d]) - k_lo;
     staged[d] = cnt <= kIndexStage;
     if (staged[d])
       for (int i = tid; i < cnt; i += kIndexThreads) s_runs[d][i] = runs[d][k_lo + i];
@@ -360,23 +364,15 @@ __global__ __launch_bounds__(kIndexThreads) void route_index_kernel(RouteDev ws,
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
     const int32_t k_lo = s_k[d][0], k_hi = s_k[d][1];
-    int32_t k;
-    RunPair r;
-    int32_t run_end;
-    if (staged[d]) {
-      k = k_lo + last_run_at_or_before(s_runs[d], 0, k_hi - k_lo + 1, row);
-      r = s_runs[d][k - k_lo];
-      run_end = k + 1 < n_runs[d] ? s_runs[d][k + 1 - k_lo].out : total;
-    } else {
-      k = last_run_at_or_before(runs[d], k_lo, k_hi + 1, row);
-      r = runs[d][k];
-      run_end = k + 1 < n_runs[d] ? runs[d][k + 1].out : total;
-    }
     DirEntry e;
-    e.in = r.in + (row - r.out);
-    e.run_end = run_end;
-    e.run = k;
-    e.pad = 0;
+    if (staged[d]) {
+      const int32_t n_staged = min(k_hi + kDirBlock + 1, n_runs[d]) - k_lo;
+      const int32_t k = last_run_at_or_before(s_runs[d], 0, k_hi - k_lo + 1, row);
+      e = dir_entry(s_runs[d], k, n_staged, row, total);
+      e.run += k_lo;
+    } else {
+      e = dir_entry(runs[d], last_run_at_or_before(runs[d], k_lo, k_hi + 1, row), n_runs[d], row, total);
+    }
     dir[d][b] = e;
   }
 }

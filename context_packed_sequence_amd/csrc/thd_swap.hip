@@ -58,9 +58,10 @@ __device__ __forceinline__ void copy_span(const U* __restrict__ src, U* __restri
 
 // One tile of output rows [r0, r1): find the run holding r0 from the
 // directory (one 16-byte load covers the usual case where no run starts
-// between the directory row, a multiple of 16, and r0), then copy run piece by
-// run piece.  Every access stays inside the run table and inside [0, total)
-// rows of both buffers.
+// between the directory row, a multiple of 16, and r0; otherwise the entry's
+// run-start bits name the run, and one load of it follows), then copy run
+// piece by run piece.  Every access stays inside the run table and inside
+// [0, total) rows of both buffers.
 template <typename U, int BLOCK, int UNROLL, bool NT>
 __device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
                                           int32_t n_runs, const unsigned char* __restrict__ in,
@@ -73,8 +74,7 @@ __device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, cons
     in_row = e.in + (r0 & (kDirBlock - 1));
     run_end = e.run_end;
   } else {
-    k = e.run + 1;
-    while (k + 1 < n_runs && runs[k + 1].out <= r0) ++k;
+    k = run_of_row(e, r0);
     if (k >= n_runs) return;
     const RunPair run = runs[k];
     if (run.out > r0) return;
@@ -108,8 +108,7 @@ __device__ __forceinline__ void swap_row_part(const RunPair* __restrict__ runs, 
   if (r < e.run_end) {
     in_row = e.in + (r & (kDirBlock - 1));
   } else {
-    int32_t k = e.run + 1;
-    while (k + 1 < n_runs && runs[k + 1].out <= r) ++k;
+    const int32_t k = run_of_row(e, r);
     if (k >= n_runs) return;
     const RunPair run = runs[k];
     if (run.out > r) return;
@@ -140,11 +139,7 @@ __device__ __forceinline__ void swap_tile_small(const RunPair* __restrict__ runs
   if (tid < 2) {  // run holding the first row and run holding the last row of the tile
     const int32_t row = tid == 0 ? r0 : r1 - 1;
     const DirEntry e = dir[row >> kDirShift];
-    int32_t k = e.run;
-    if (row >= e.run_end) {
-      k = e.run + 1;
-      while (k + 1 < n_runs && runs[k + 1].out <= row) ++k;
-    }
+    const int32_t k = row < e.run_end ? e.run : run_of_row(e, row);
     s_k[tid] = min(k, n_runs - 1);
   }
   __syncthreads();
