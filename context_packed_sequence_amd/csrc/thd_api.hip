@@ -200,7 +200,7 @@ int thd_copy(const void* in, void* out, int64_t bytes, void* stream) {
   if (bytes == 0) return THD_OK;
   if (!in || !out) return THD_ERR_ARG;
   if (overlaps(in, bytes, out, bytes)) return THD_ERR_ALIAS;
-  if (thdcp::launch_copy(in, out, bytes, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
+  if (thdcp::launch_copy(in, out, bytes, g_swap_cfg, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
   return THD_OK;
 }
 

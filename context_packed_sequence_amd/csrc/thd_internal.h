@@ -78,11 +78,13 @@ struct SwapLaunch {
   int32_t block_threads;  // 128, 256, 512 or 1024
   int32_t tile_order;     // tiles per XCD chunk: 1 natural order, G > 1 XCD-chunked
 };
+
+// Plain streaming copy (thd_copy); cfg.block_threads and cfg.tile_order apply.
+hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunch& cfg, hipStream_t stream);
 hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                        const void* in, void* out, int32_t total, int64_t row_bytes,
                        const SwapLaunch& cfg, hipStream_t stream);
 
-hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t stream);
 hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                              int32_t n, const void* const* ins, void* const* outs, const int64_t* row_bytes,
                              int32_t total, hipStream_t stream);

@@ -208,13 +208,20 @@ __global__ __launch_bounds__(BLOCK) void swap_kernel(const int32_t* __restrict__
                                                      const unsigned char* __restrict__ in,
                                                      unsigned char* __restrict__ out, int32_t total,
                                                      int64_t row_bytes, int32_t tile_rows, int32_t n_tiles,
-                                                     int32_t chunk, int32_t n_slots) {
+                                                     int32_t chunk, int32_t n_slots, int32_t parts,
+                                                     int64_t part_bytes) {
   if (hdr[kHdrStatus] != THD_OK) return;  // a failed build writes nothing
   const int32_t n_runs = hdr[runs_word];
   for (int32_t slot = blockIdx.x; slot < n_slots; slot += gridDim.x) {
     const int32_t x = slot % kXcds, j = slot / kXcds;
     const int32_t tile = chunk == 1 ? slot : ((j / chunk) * kXcds + x) * chunk + j % chunk;
     if (tile >= n_tiles) continue;
+    if (parts > 1) {  // rows cut into slices: tile = (row, slice)
+      const int32_t r = tile / parts;
+      const int64_t b0 = static_cast<int64_t>(tile - r * parts) * part_bytes;
+      swap_row_part<U, BLOCK, UNROLL, NT>(runs, dir, n_runs, in, out, row_bytes, r, b0, min(row_bytes, b0 + part_bytes));
+      continue;
+    }
     const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(tile) * tile_rows);
     const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + tile_rows));
     swap_tile<U, BLOCK, UNROLL, NT>(runs, dir, n_runs, in, out, total, row_bytes, r0, r1);
@@ -240,6 +247,8 @@ struct BatchArgs {
   BatchTensor t[THD_MAX_BATCH];
   int32_t n;
   int32_t total_tiles;
+  int32_t chunk;    // tiles per XCD chunk (1: natural order), as in swap_kernel
+  int32_t n_slots;  // workgroup slots: total_tiles rounded up to whole chunk rounds
 };
 
 constexpr int kBatchBlock = 128;
@@ -252,7 +261,10 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
   __shared__ int32_t s_k[2];
   if (hdr[kHdrStatus] != THD_OK) return;
   const int32_t n_runs = hdr[runs_word];
-  for (int32_t g = blockIdx.x; g < args.total_tiles; g += gridDim.x) {
+  for (int32_t slot = blockIdx.x; slot < args.n_slots; slot += gridDim.x) {
+    const int32_t x = slot % kXcds, j = slot / kXcds;
+    const int32_t g = args.chunk == 1 ? slot : ((j / args.chunk) * kXcds + x) * args.chunk + j % args.chunk;
+    if (g >= args.total_tiles) continue;
     int i = 0;
     while (i + 1 < args.n && args.t[i + 1].first_tile <= g) ++i;
     const BatchTensor bt = args.t[i];
@@ -285,15 +297,20 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
   }
 }
 
-// Plain streaming copy of whole tiles: no route, no permutation.  The same
-// units, workgroup shape and non-temporal accesses as the swap's streaming
-// path, so a swap can be compared with a copy of the same bytes.
+// Plain streaming copy of 4 KiB tiles: no route, no permutation.  The swap's
+// units, tiles and non-temporal accesses; 128 threads in XCD-chunked order
+// with chunks of 256 tiles, the fastest plain-copy shape in sweeps on
+// MI355X (the swap's workgroup size and tile order from thd_swap_tuning
+// apply here too, for sweeps).
 template <typename U, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void copy_kernel(const unsigned char* __restrict__ in,
                                                      unsigned char* __restrict__ out, int64_t bytes,
-                                                     int64_t tile_bytes) {
-  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * tile_bytes;
-  if (b0 >= bytes) return;
+                                                     int64_t tile_bytes, int32_t n_tiles, int32_t chunk) {
+  const int32_t slot = blockIdx.x;
+  const int32_t x = slot % kXcds, j = slot / kXcds;
+  const int32_t tile = chunk == 1 ? slot : ((j / chunk) * kXcds + x) * chunk + j % chunk;
+  if (tile >= n_tiles) return;
+  const int64_t b0 = static_cast<int64_t>(tile) * tile_bytes;
   const int64_t n = min(tile_bytes, bytes - b0) / static_cast<int64_t>(sizeof(U));
   copy_span<U, BLOCK, UNROLL, true>(reinterpret_cast<const U*>(in + b0), reinterpret_cast<U*>(out + b0), n);
 }
@@ -307,7 +324,8 @@ int copy_unit(int64_t row_bytes, const void* in, const void* out) {
 }
 
 struct Shape {
-  int32_t tile_rows, n_tiles, chunk, n_slots, grid;
+  int32_t tile_rows, n_tiles, chunk, n_slots, grid, parts;
+  int64_t part_bytes;
 };
 
 template <typename U, int BLOCK, int UNROLL>
@@ -317,10 +335,12 @@ hipError_t launch_typed(const int32_t* hdr, const RunPair* runs, int runs_word, 
   auto* o8 = static_cast<unsigned char*>(out);
   if (nt)
     hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, true>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr, runs_word,
-                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots);
+                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots, sh.parts,
+                       sh.part_bytes);
   else
     hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, false>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr, runs_word,
-                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots);
+                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots, sh.parts,
+                       sh.part_bytes);
   return hipGetLastError();
 }
 
@@ -355,22 +375,37 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
     return hipGetLastError();
   }
 
-  // Launch shape.  Measured on MI355X: the swap streams best when each
-  // workgroup copies about one row -- 4 KiB tiles of 128 threads in natural
-  // order for rows under 8 KiB; one row per 512-thread workgroup in
-  // XCD-chunked order (chunks of 64 tiles) for rows of 8 KiB and more.  Every
-  // field can be overridden for sweeps.
+  // Launch shape.  Measured on MI355X (head-to-head sweeps on one box,
+  // repeated on a second): every workgroup moves about 4 KiB.  Rows of 4 KiB
+  // up to 8 KiB: one row per 256-thread workgroup, XCD-chunked order with
+  // chunks of 128 tiles.  Rows of 8 KiB and more: 4 KiB slices of one row per
+  // 128-thread workgroup, chunks of 64.  Shorter rows: 4 KiB tiles of whole
+  // rows, 128 threads, natural order.  Every field can be overridden for
+  // sweeps; a tile size below the row size cuts rows into slices.
   const bool big_rows = unit == 16 && row_bytes >= 8192;
-  const int64_t tile_bytes = cfg.tile_bytes > 0 ? cfg.tile_bytes : (big_rows ? row_bytes : (unit == 16 ? 4096 : 8192));
-  const int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (big_rows ? 512 : 128) : 256);
-  int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order : (big_rows ? 64 : 1);
+  const bool mid_rows = unit == 16 && row_bytes >= 4096 && !big_rows;
+  const int64_t tile_bytes =
+      cfg.tile_bytes > 0 ? cfg.tile_bytes : (mid_rows ? row_bytes : (unit == 16 ? 4096 : 8192));
+  const int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (mid_rows ? 256 : 128) : 256);
+  int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order : (big_rows ? 64 : (mid_rows ? 128 : 1));
 
   int64_t tile_rows = (tile_bytes + row_bytes - 1) / row_bytes;
   if (tile_rows < 1) tile_rows = 1;
   if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
   Shape sh;
   sh.tile_rows = static_cast<int32_t>(tile_rows);
-  sh.n_tiles = static_cast<int32_t>((total + tile_rows - 1) / tile_rows);
+  sh.parts = 1;
+  sh.part_bytes = row_bytes;
+  int64_t n_tiles = (total + tile_rows - 1) / tile_rows;
+  if (unit == 16 && tile_bytes < row_bytes) {  // tiles are slices of one row
+    int64_t parts = (row_bytes + tile_bytes - 1) / tile_bytes;
+    sh.part_bytes = ((row_bytes + parts - 1) / parts + 15) / 16 * 16;
+    parts = (row_bytes + sh.part_bytes - 1) / sh.part_bytes;
+    n_tiles = static_cast<int64_t>(total) * parts;
+    if (parts > INT32_MAX || n_tiles > INT32_MAX) return hipErrorInvalidValue;
+    sh.parts = static_cast<int32_t>(parts);
+  }
+  sh.n_tiles = static_cast<int32_t>(n_tiles);
   const int64_t per_xcd = (sh.n_tiles + kXcds - 1) / kXcds;
   if (chunk > per_xcd) chunk = per_xcd > 0 ? per_xcd : 1;  // one chunk per XCD at most
   sh.chunk = static_cast<int32_t>(chunk);
@@ -434,27 +469,52 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   args.total_tiles = static_cast<int32_t>(tiles);
-  hipLaunchKernelGGL(swap_batch_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kBatchBlock), 0, stream, hdr,
+  // XCD-chunked tile order (chunks of 64 tiles of about 4 KiB), as the
+  // single-tensor swap uses for long rows
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+  args.chunk = static_cast<int32_t>(per_xcd < 64 ? per_xcd : 64);
+  const int64_t slots = args.chunk == 1 ? tiles : (tiles + kXcds * args.chunk - 1) / (kXcds * args.chunk) * kXcds * args.chunk;
+  if (slots > INT32_MAX) return hipErrorInvalidValue;
+  args.n_slots = static_cast<int32_t>(slots);
+  hipLaunchKernelGGL(swap_batch_kernel, dim3(static_cast<unsigned>(slots)), dim3(kBatchBlock), 0, stream, hdr,
                      runs_word, runs, dir, total, args);
   return hipGetLastError();
 }
 
-hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t stream) {
+hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunch& cfg, hipStream_t stream) {
   const int unit = copy_unit(bytes, in, out);
   const int64_t tile_bytes = unit == 16 ? 4096 : 8192;
   const int64_t tiles = (bytes + tile_bytes - 1) / tile_bytes;
   if (tiles <= 0) return hipSuccess;
-  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+  const int32_t n_tiles = static_cast<int32_t>(tiles);
+  int32_t chunk = cfg.tile_order > 0 ? min(cfg.tile_order, static_cast<int32_t>(INT32_MAX / 16)) : (unit == 16 ? 256 : 1);
+  const int32_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
+  if (chunk > per_xcd) chunk = per_xcd;
+  const int64_t slots =
+      chunk == 1 ? n_tiles : (static_cast<int64_t>(n_tiles) + kXcds * chunk - 1) / (kXcds * chunk) * kXcds * chunk;
+  if (slots > INT32_MAX) return hipErrorInvalidValue;
   const auto* i8 = static_cast<const unsigned char*>(in);
   auto* o8 = static_cast<unsigned char*>(out);
-  const dim3 grid(static_cast<unsigned>(tiles));
+  const dim3 grid(static_cast<unsigned>(slots));
+  const int block = unit == 16 && cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? 128 : 256);
+#define THD_COPY(U_, B_, R_) \
+  hipLaunchKernelGGL((copy_kernel<U_, B_, R_>), grid, dim3(B_), 0, stream, i8, o8, bytes, tile_bytes, n_tiles, chunk)
   switch (unit) {
-    case 16: hipLaunchKernelGGL((copy_kernel<u32x4, 128, 8>), grid, dim3(128), 0, stream, i8, o8, bytes, tile_bytes); break;
-    case 8: hipLaunchKernelGGL((copy_kernel<u32x2, 256, 4>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
-    case 4: hipLaunchKernelGGL((copy_kernel<uint32_t, 256, 8>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
-    case 2: hipLaunchKernelGGL((copy_kernel<uint16_t, 256, 8>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
-    default: hipLaunchKernelGGL((copy_kernel<uint8_t, 256, 8>), grid, dim3(256), 0, stream, i8, o8, bytes, tile_bytes); break;
+    case 16:
+      switch (block) {
+        case 256: THD_COPY(u32x4, 256, 4); break;
+        case 512: THD_COPY(u32x4, 512, 2); break;
+        case 1024: THD_COPY(u32x4, 1024, 2); break;
+        default: THD_COPY(u32x4, 128, 8); break;
+      }
+      break;
+    case 8: THD_COPY(u32x2, 256, 4); break;
+    case 4: THD_COPY(uint32_t, 256, 8); break;
+    case 2: THD_COPY(uint16_t, 256, 8); break;
+    default: THD_COPY(uint8_t, 256, 8); break;
   }
+#undef THD_COPY
   return hipGetLastError();
 }
 

@@ -283,17 +283,21 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
  * in this process (a process-wide setting; not safe to change while another
  * thread calls thd_swap).  For launch-shape sweeps: the results of thd_swap
  * never depend on it.  A 0 selects the built-in choice for that field.
- *   tile_bytes      output bytes per workgroup tile, rounded up to whole rows
- *                   (built-in: 4 KiB for rows under 8 KiB, one row otherwise)
+ *   tile_bytes      output bytes per workgroup tile, rounded up to whole rows;
+ *                   with 16-byte units, a value below the row size cuts each
+ *                   row into slices of about that size (built-in: 4 KiB of
+ *                   whole rows under 4 KiB, one row for rows of 4 KiB up to
+ *                   8 KiB, 4 KiB slices for rows of 8 KiB and more)
  *   max_workgroups  cap on workgroups; above it workgroups loop over tiles
  *   nontemporal     1: non-temporal loads and stores (built-in), 0: plain
- *   block_threads   128, 256, 512 or 1024 for the 16-byte path
+ *   block_threads   128, 256, 512 or 1024 for the 16-byte path (built-in:
+ *                   256 for rows of 4 KiB up to 8 KiB, 128 otherwise)
  *   tile_order      tiles per XCD chunk: 1 = natural order (tile b to
  *                   workgroup b, so neighbouring tiles go to different
  *                   XCDs); G > 1 = XCD-chunked (tiles cut into chunks of G,
  *                   XCD x streams chunks x, x+8, ...; G >= tiles / 8
- *                   gives each XCD one contiguous eighth); built-in: 1
- *                   for rows under 8 KiB, 64 otherwise
+ *                   gives each XCD one contiguous eighth); built-in: 128
+ *                   for rows of 4 KiB up to 8 KiB, 64 above, 1 below
  * thd_swap_tuning(0, 0, 1, 0, 0) restores the built-in shape.
  */
 int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
@@ -302,9 +306,12 @@ int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontempo
 /*
  * thd_copy -- plain streaming copy of `bytes` bytes from `in` to `out`
  * (device pointers, non-overlapping): no route, no permutation.  It moves
- * the bytes with the same 16-byte non-temporal units and workgroup shape as
- * thd_swap, so a swap's bandwidth can be set beside that of a copy of the
- * same bytes in the same run.  Stream-ordered, one launch; THD_ERR_ARG for a
+ * the bytes in 4 KiB tiles with the same 16-byte non-temporal units as
+ * thd_swap, in the launch shape that streams a plain copy fastest (128
+ * threads per tile, XCD-chunked order with chunks of 256 tiles; the
+ * block_threads and tile_order of thd_swap_tuning override it), so a
+ * swap's bandwidth can be set beside that of a copy of the same bytes in
+ * the same run.  Stream-ordered, one launch; THD_ERR_ARG for a
  * negative size or a null pointer (bytes > 0), THD_ERR_ALIAS for overlapping
  * buffers; 0 bytes is THD_OK with no launch.
  */

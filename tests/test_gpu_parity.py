@@ -120,6 +120,8 @@ def test_random_swap_parity(thd, case):
     (0, 0, 1, 0, 0, 4096), (0, 6, 1, 0, 0, 4096), (0, 0, 1, 0, 2, 2048), (5000, 0, 1, 0, 2, 36),
     (0, 7, 1, 0, 0, 8), (0, 3, 1, 0, 0, 1), (0, 0, 0, 0, 0, 16), (0, 5, 1, 0, 0, 2),
     (4096, 0, 1, 128, 64, 4096), (8192, 0, 1, 512, 3, 8192), (0, 11, 1, 0, 1 << 30, 8192), (0, 0, 1, 0, 7, 48),
+    # rows cut into slices (tile_bytes below the row size)
+    (4096, 0, 1, 128, 1, 8192), (2048, 0, 1, 128, 64, 8192), (3000, 9, 0, 256, 1, 8208), (16, 0, 1, 128, 5, 4096),
 ])
 def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt, block, order, rb):
     import torch
