@@ -94,4 +94,28 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
   __syncthreads();
 }
 
+// Division of a non-negative int32 by a divisor that is fixed for a whole
+// kernel: one multiply-high, an add and two shifts instead of the integer
+// division sequence.  Round-up method of Granlund and Montgomery ("Division
+// by Invariant Integers using Multiplication", 1994, Figure 4.1) with
+// N = 32: l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, then
+// floor(n / d) = (t + ((n - t) >> 1)) >> (l - 1) with t = mulhi(m, n).
+// Valid for 0 <= n < 2^31 and 1 <= d < 2^31.
+struct FastDiv {
+  uint32_t m;
+  int l;
+  __device__ static FastDiv make(int32_t d) {
+    FastDiv f{0, 0};
+    while ((1u << f.l) < static_cast<uint32_t>(d)) ++f.l;
+    const uint64_t num = (uint64_t{1} << 32) * ((uint64_t{1} << f.l) - static_cast<uint64_t>(d));
+    f.m = static_cast<uint32_t>(num / static_cast<uint64_t>(d) + 1);
+    return f;
+  }
+  __device__ __forceinline__ int32_t operator()(int32_t n) const {
+    if (l == 0) return n;  // d == 1
+    const uint32_t t = __umulhi(m, static_cast<uint32_t>(n));
+    return static_cast<int32_t>((t + ((static_cast<uint32_t>(n) - t) >> 1)) >> (l - 1));
+  }
+};
+
 }  // namespace thdcp

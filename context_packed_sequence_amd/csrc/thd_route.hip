@@ -67,17 +67,29 @@ struct Cut {
   int32_t first_d, rem, pieces;
 };
 
-__device__ __forceinline__ Cut cut_segment(const Segment& s, int32_t share) {
+__device__ __forceinline__ Cut cut_segment(const Segment& s, int32_t share, const FastDiv& div_share) {
   Cut c;
-  c.first_d = s.tok / share;
+  c.first_d = div_share(s.tok);
   c.rem = s.tok - c.first_d * share;
   c.pieces = (c.rem + s.len > share) ? 2 : 1;
   return c;
 }
 
-// The build kernel keeps the compacted documents and the split matrix in LDS
-// when 4 * (3 * n_slots + cp * cp) bytes fit in kBuildLdsBytes; otherwise it
-// uses the route's global scratch and global atomics (same steps, slower).
+// The LDS split matrix is kept in several copies while the segments are
+// counted: lane l adds into copy l mod copies, because the lanes of a wave
+// mostly hit the same few (source, destination) entries and atomics from many
+// lanes to one LDS address serialise.  The copies are summed afterwards.
+constexpr int kSplitEntries = 1024;  // cp * cp * copies stays within this
+__host__ __device__ inline int split_copies(int32_t cp) {
+  const int64_t sq = static_cast<int64_t>(cp) * cp;
+  if (sq >= kSplitEntries) return 1;
+  const int c = static_cast<int>(kSplitEntries / sq);
+  return c > 16 ? 16 : c;
+}
+
+// The build kernel keeps the compacted documents and the split matrix (in
+// split_copies(cp) copies) in LDS when they fit in kBuildLdsBytes; otherwise
+// it uses the route's global scratch and global atomics (same steps, slower).
 constexpr int kBuildLdsBytes = 60 * 1024;
 
 // Fused build: when the runs of both orders fit in LDS as well, every
@@ -117,21 +129,25 @@ template <bool kLds, bool kFused>
 __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
                                                                     int32_t cp, int32_t total, RouteDev ws,
                                                                     int32_t lds_run_cap) {
-  // kLds: docs[3 * n_slots], split[cp * cp]; kFused adds, 8-byte aligned,
-  // runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
+  // kLds: docs[3 * n_slots], split[copies * cp * cp]; kFused adds, 8-byte
+  // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
   extern __shared__ int32_t s_dyn[];
   __shared__ int s_wave[kBuildWaves + 1];
   __shared__ int s_sev;
+  __shared__ FastDiv s_div[3];  // by share, 2 * n_docs, 2 * cp
   const int tid = threadIdx.x;
   const bool writer = !kFused || blockIdx.x == 0;  // the workgroup that writes the route out
   const int32_t cap = kLds ? n_slots : ws.docs_cap;
+  const int32_t cp2 = cp * cp;
+  const int copies = kLds ? split_copies(cp) : 1;
   int32_t* docs = kLds ? s_dyn : ws.docs;
   int32_t* split = kLds ? s_dyn + 3 * n_slots : ws.split;
-  RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + cp * cp + 1) & ~1));
+  int32_t* my_split = split + (threadIdx.x & 63) % copies * cp2;  // this lane's copy
+  RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + copies * cp2 + 1) & ~1));
   RunPair* l_dst = l_src + lds_run_cap;
 
   if (tid == 0) s_sev = 0;
-  for (int i = tid; i < cp * cp; i += kBuildThreads) {
+  for (int i = tid; i < copies * cp2; i += kBuildThreads) {
     if constexpr (kLds) split[i] = 0;
     else __hip_atomic_store(&split[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -166,6 +182,11 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     n_docs += sum;
   }
   if (sev) atomicMax(&s_sev, sev);
+  if (tid == 0) {
+    s_div[0] = FastDiv::make(total / cp > 0 ? total / cp : 1);
+    s_div[1] = FastDiv::make(n_docs > 0 ? 2 * n_docs : 1);
+    s_div[2] = FastDiv::make(two_cp);
+  }
   if constexpr (!kLds) __threadfence();  // global path: zeroed split and document list are complete
   __syncthreads();                       // publishes the document list to the whole workgroup
   if (s_sev) {
@@ -186,6 +207,9 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   const int32_t n_seg = two_cp * n_docs;
   const int32_t two_n = 2 * n_docs;
   bool overflow = false;
+  // the loop below divides by these three on every segment (set up once by
+  // thread 0 before the barrier that publishes the documents)
+  const FastDiv div_share = s_div[0], div_two_n = s_div[1], div_two_cp = s_div[2];
 
   // ---- 3+4. runs in zigzag-row order (with the split matrix) and in token
   //           order.  Thread j looks at segment j of each order, counts the
@@ -199,24 +223,24 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     Cut cs{0, 0, 0}, ct{0, 0, 0};
     if (j < n_seg) {
       // zigzag-row order: rank-major, then document, then front/back chunk
-      const int32_t r = j / two_n;
+      const int32_t r = div_two_n(j);
       const int32_t rem = j - r * two_n;
       const int32_t k = rem >> 1;
       const bool back = rem & 1;
       const Doc dk = load_doc(docs, cap, k);
       ss = chunk_segment(dk, back ? two_cp - 1 - r : r, cp, share);
-      cs = cut_segment(ss, share);
+      cs = cut_segment(ss, share, div_share);
       if (rem > 0 && cs.rem != 0) {  // not the first row of a source share, not on a destination border
         const Doc dp = back ? dk : load_doc(docs, cap, k - 1);
         const Segment p = chunk_segment(dp, back ? r : two_cp - 1 - r, cp, share);
         merge_s = (p.tok + p.len == ss.tok) ? 1 : 0;
       }
       // token order: document-major, then chunk
-      const int32_t kt = j / two_cp;
+      const int32_t kt = div_two_cp(j);
       const int32_t q = j - kt * two_cp;
       const Doc dt = load_doc(docs, cap, kt);
       st = chunk_segment(dt, q, cp, share);
-      ct = cut_segment(st, share);
+      ct = cut_segment(st, share, div_share);
       if (j > 0 && !(kt == 0 && q < cp) && ct.rem != 0) {
         const Doc dp = q > 0 ? dt : load_doc(docs, cap, kt - 1);
         const Segment p = chunk_segment(dp, q > 0 ? q - 1 : two_cp - 1, cp, share);
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
       for (int p = 0; p < cs.pieces; ++p) {
         const int32_t ptok = p == 0 ? ss.tok : (cs.first_d + p) * share;
         const int32_t pend = min(ss.tok + ss.len, (cs.first_d + p + 1) * share);
-        atomicAdd(&split[ss.rank * cp + cs.first_d + p], pend - ptok);
+        atomicAdd(&my_split[ss.rank * cp + cs.first_d + p], pend - ptok);
         if (p >= merge_s) {
           const int64_t slot = static_cast<int64_t>(n_src) + off_s + p - merge_s;
           const RunPair run{ss.src + (ptok - ss.tok), ptok};
@@ -259,6 +283,14 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   }
   if constexpr (!kLds) __threadfence();  // global path: every split atomic has landed
   __syncthreads();
+  if (copies > 1) {  // fold the copies into the first
+    for (int i = tid; i < cp2; i += kBuildThreads) {
+      int32_t v = split[i];
+      for (int c = 1; c < copies; ++c) v += split[c * cp2 + i];
+      split[i] = v;
+    }
+    __syncthreads();
+  }
 
   // ---- 5. integrity: same run count both ways; each rank sends and receives T/cp ----
   bool bad = overflow || n_src != n_dst;
@@ -379,19 +411,25 @@ __global__ __launch_bounds__(kIndexThreads) void route_index_kernel(RouteDev ws,
 
 }  // namespace
 
+// Dynamic LDS of the build kernel: documents and split copies (int32), and,
+// fused, the runs of both orders (8-byte aligned).
+int64_t build_lds_bytes(int32_t n_slots, int32_t cp, bool fused) {
+  const int64_t words = 3LL * n_slots + static_cast<int64_t>(split_copies(cp)) * cp * cp;
+  if (!fused) return 4 * words;
+  return 4 * ((words + 1) & ~1LL) + 16 * (2LL * cp * n_slots + cp);
+}
+
 bool route_build_fused(int32_t n_slots, int32_t cp) {
   const int64_t segments = 2LL * cp * n_slots;
-  const int64_t run_cap = segments + cp;
-  const int64_t lds = 4 * ((3LL * n_slots + static_cast<int64_t>(cp) * cp + 1) & ~1LL) + 16 * run_cap;
-  return segments <= kFusedMaxSegments && lds <= kBuildLdsBytes;
+  return segments <= kFusedMaxSegments && build_lds_bytes(n_slots, cp, true) <= kBuildLdsBytes;
 }
 
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total, const RouteDev& ws,
                               hipStream_t stream) {
-  const int64_t lds = 4 * (3 * static_cast<int64_t>(n_slots) + static_cast<int64_t>(cp) * cp);
+  const int64_t lds = build_lds_bytes(n_slots, cp, false);
   if (route_build_fused(n_slots, cp)) {
     const int32_t run_cap = 2 * cp * n_slots + cp;
-    const int64_t lds_fused = 4 * ((3LL * n_slots + static_cast<int64_t>(cp) * cp + 1) & ~1LL) + 16LL * run_cap;
+    const int64_t lds_fused = build_lds_bytes(n_slots, cp, true);
     const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
     const int32_t grid = n_blocks > 0 ? (n_blocks + kDirPerFusedGroup - 1) / kDirPerFusedGroup : 1;
     hipLaunchKernelGGL((route_build_kernel<true, true>), dim3(grid), dim3(kBuildThreads),
