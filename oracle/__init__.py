@@ -23,7 +23,8 @@ Pins (each function is checked against something other than itself in
   round-trip and cp=1 identities;
 * label shift / MTP roll / valid mask: the valid mask and the 13-token count
   printed in §3.4 / §3.8, per-shift closed-form counts, and a per-document
-  ``numpy.roll`` on unpadded documents;
+  ``numpy.roll`` on unpadded documents; the single-position form
+  (``roll_valid_at``) against the whole-batch one on every small case;
 * packing: the boundaries, padding and packed stream printed in §3.2-§3.4 of
   the same page, plus hand-worked corner cases (all-pad rows, PAD inside a
   document, rows ending in EOD, a last document without EOD).
@@ -46,5 +47,6 @@ from .thd_oracle import (  # noqa: F401
     canonical_runs,
     swap_rows,
     roll_labels,
+    roll_valid_at,
     pack_batch,
 )

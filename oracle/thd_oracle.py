@@ -357,6 +357,24 @@ def roll_labels(ids, cu_padded, cu_real, total: int, max_shift: int, fill: int =
     return shifted, mask
 
 
+def roll_valid_at(cu_padded, cu_real, token: int, shift: int) -> bool:
+    """Whether shift ``shift`` of one position is a real label, for checking
+    huge batches one position at a time.
+
+    The same definition as ``roll_labels`` read for a single position: the
+    padded slot holding ``token`` ends its real tokens at
+    ``e = cu_padded[s] + (cu_real[s+1] - cu_real[s])``, and shift j is valid
+    when ``token + j < e`` (shift 0 is the valid-token mask).  The shifted
+    value is then ``ids[token + j]``, else the fill value.
+    """
+    p = _as_int_list(cu_padded)
+    r = p if cu_real is None else _as_int_list(cu_real)
+    for s in range(len(p) - 1):
+        if p[s] <= token < p[s + 1]:
+            return token + shift < p[s] + (r[s + 1] - r[s])
+    raise OracleInputError("ARG", f"position {token} outside the batch")
+
+
 # ---------------------------------------------------------------------------
 # Packing ("Packed Sequence 与上下文并行" §2.2 steps (1)-(3), §3.2-§3.4).
 # ---------------------------------------------------------------------------

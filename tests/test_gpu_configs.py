@@ -169,3 +169,58 @@ def test_maximum_size_swap(thd):
     assert torch.equal(back, x)
     del x, out, back, route
     torch.cuda.empty_cache()
+
+
+def test_maximum_size_roll(thd):
+    # T = 2**31 - 64 positions, two shifts: the label and MTP outputs reach
+    # 2 x 16 GiB, so every index past 2**31 is exercised.  Checked at sampled
+    # positions (random ones and every position near a slot's real end and
+    # padded end) with the oracle's single-position form, in natural order
+    # and written in the zigzag order of a cp = 2 route.
+    import torch
+    cp, j_max, fill = 2, 2, -5
+    total = 2 ** 31 - 64
+    lens = [1 << 29, 123456788, 4, 1000000000, 0]
+    lens[-1] = total - sum(lens[:-1])
+    real = [lens[0] - 3, lens[1], 1, lens[3] - 2, lens[4] - 1]
+    cu, cu_r = W.cumulative(lens), W.cumulative(real)
+    say("maximum size roll", total)
+    g = torch.Generator(device="cuda").manual_seed(W.BASE_SEED + 31)
+    ids = torch.randint(0, 32000, (total,), dtype=torch.int64, device="cuda", generator=g)
+    rng = np.random.default_rng(4)
+    edges = []
+    for s in range(len(lens)):
+        e = int(cu[s]) + real[s]
+        edges += [int(cu[s]), int(cu[s]) + 1, e - 3, e - 2, e - 1, e, int(cu[s + 1]) - 1]
+    toks = np.unique(np.clip(np.concatenate([rng.integers(0, total, 3000), edges, [0, total - 1]]), 0, total - 1))
+    toks_t = torch.from_numpy(toks).cuda()
+    # ids the labels may read: t + j for every sampled t and shift
+    ahead = {j: ids.index_select(0, torch.from_numpy(np.minimum(toks + j, total - 1)).cuda()).cpu().numpy()
+             for j in range(1, j_max + 1)}
+    valid = {j: np.array([O.roll_valid_at(cu, cu_r, int(t), j) for t in toks]) for j in range(j_max + 1)}
+
+    def check(shifted, mask, rows):
+        rows_t = torch.from_numpy(rows).cuda()
+        for j in range(j_max + 1):
+            assert np.array_equal(mask[j].index_select(0, rows_t).cpu().numpy(), valid[j].astype(np.uint8)), j
+            if j:
+                want = np.where(valid[j], ahead[j], fill)
+                assert np.array_equal(shifted[j - 1].index_select(0, rows_t).cpu().numpy(), want), j
+
+    shifted, mask, status = thd.roll_labels(ids, dev_i32(cu), dev_i32(cu_r), j_max, fill)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check(shifted, mask, toks)
+    assert int(mask[0].sum(dtype=torch.int64).item()) == sum(real)
+    del shifted, mask
+    torch.cuda.empty_cache()
+
+    route = thd.Route(len(lens), cp, total)
+    route.build(dev_i32(cu), cp, total)
+    shifted, mask, status = route.roll_labels_zigzag(ids, dev_i32(cu), dev_i32(cu_r), j_max, fill)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rows = np.array([O.zigzag_position(cu, cp, total, int(t)) for t in toks], dtype=np.int64)
+    check(shifted, mask, rows)
+    del shifted, mask, ids, route
+    torch.cuda.empty_cache()

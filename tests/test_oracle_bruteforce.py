@@ -262,3 +262,28 @@ def test_workload_recipes():
     assert W.make("long1m").n_slots == 6
     # seeded: the same recipe gives the same batch
     assert np.array_equal(W.make("full").cu_padded, W.make("full").cu_padded)
+
+
+def test_single_position_roll_form_matches_the_batch_form():
+    # roll_valid_at (used to check huge batches position by position) against
+    # roll_labels on random small batches with pads, empty slots and every shift.
+    rng = np.random.default_rng(11)
+    for _ in range(60):
+        n = int(rng.integers(1, 7))
+        padded = [int(rng.integers(0, 6)) * 4 for _ in range(n)]
+        real = [int(rng.integers(0, p + 1)) for p in padded]
+        cu_p = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+        cu_r = np.concatenate([[0], np.cumsum(real)]).astype(np.int64)
+        total = int(cu_p[-1])
+        if total == 0:
+            continue
+        ids = rng.integers(0, 1000, size=total)
+        shifted, mask = O.roll_labels(ids, cu_p, cu_r, total, 4, -7)
+        for t in range(total):
+            for j in range(5):
+                ok = O.roll_valid_at(cu_p, cu_r, t, j)
+                assert mask[j, t] == ok, (cu_p, cu_r, t, j)
+                if j:
+                    assert shifted[j - 1, t] == (ids[t + j] if ok else -7)
+    with pytest.raises(O.OracleInputError):
+        O.roll_valid_at([0, 4], [0, 4], 4, 0)

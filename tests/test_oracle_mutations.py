@@ -127,7 +127,21 @@ def _pack_valid_end_at_first_pad(tokens, pad_id, eod_id, align, capacity, max_do
     return _real_pack(rows, pad_id, eod_id, align, capacity, max_docs, pad_value)
 
 
+_real_roll_at = T.roll_valid_at
+
+
+def _roll_at_inclusive_end(cu_padded, cu_real, token, shift):   # t + j <= e instead of t + j < e
+    return _real_roll_at(cu_padded, cu_real, token, shift - 1) if shift > 0 else _real_roll_at(
+        cu_padded, cu_real, token, shift)
+
+
+def _roll_at_padded_end(cu_padded, cu_real, token, shift):      # real lengths ignored
+    return _real_roll_at(cu_padded, None, token, shift)
+
+
 MUTATIONS = {
+    "single-position roll: label reaches one past the end": ("roll_valid_at", _roll_at_inclusive_end),
+    "single-position roll: real lengths ignored": ("roll_valid_at", _roll_at_padded_end),
     "pack: EOD opens the next document": ("pack_batch", _pack_eod_starts_next),
     "pack: document after the last EOD dropped": ("pack_batch", _pack_drops_trailing),
     "pack: valid part ends at the first PAD": ("pack_batch", _pack_valid_end_at_first_pad),
@@ -171,6 +185,7 @@ def run_pins():
         ("brute force", lambda: [BF.test_zigzag_matches_sort_key_and_closed_form(cp) for cp in (2, 3)]),
         ("a2a", lambda: BF.test_emulated_all_to_all_matches_global_swap(2)),
         ("np.roll", BF.test_roll_matches_per_document_numpy_roll),
+        ("single-position roll", BF.test_single_position_roll_form_matches_the_batch_form),
         ("no crossing", lambda: BF.test_roll_counts_and_no_crossing(1)),
         ("pack example", lambda: P.test_pack_reproduces_the_worked_example(worked)),
         ("pack budget", P.test_pack_budget_and_empty_slots),
