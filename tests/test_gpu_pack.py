@@ -53,6 +53,7 @@ CASES = [
     (6, 1200, 17, 0.1, None, 0.1, 8, 1000, 10),    # many short rows
     (7, 2, 3072, 0.001, 1024, 0.0, 512, 3, 2),      # rows of whole 1024-token chunks, wide alignment
     (8, 3, 2048, 0.0, 1, 0.0, 3, 5, 1),             # one document per row crossing chunks, odd alignment
+    (9, 3000, 1500, 0.002, 300, 0.01, 8, 10, 5),    # 6000 chunks: the scan carries across six passes
 ]
 
 
@@ -185,3 +186,21 @@ def test_pack_route_roll_swap_chain(thd, cp, seed):
         assert np.array_equal(mask[k].cpu().numpy(), O.swap_rows(wm_[k], want_cup, cp, capacity, "c2z"))
     assert np.array_equal(zig_tokens.cpu().numpy(), O.swap_rows(want_packed, want_cup, cp, capacity, "c2z"))
     assert np.array_equal(zig_pos.cpu().numpy(), O.layout_tokens(want_cup, cp, capacity, O.ZIGZAG))
+
+
+@pytest.mark.parametrize("batch,seq,align", [(16, 8192, 8), (16, 16384, 32), (16, 65536, 8)])
+def test_pack_at_bench_sizes(thd, batch, seq, align):
+    # The inputs and launch the bench times for the 128K, full and 1M
+    # batches ([16, T/16] rows, 256 document slots), compared in full.
+    import torch
+    max_docs = 256
+    rows = W.token_rows(7, batch, seq, PAD, EOD, 1.0 / 4096, 512)
+    capacity = ((batch * seq) // align + max_docs + 1) * align
+    say("pack bench size", batch, seq, align)
+    want = O.pack_batch(rows, PAD, EOD, align, capacity, max_docs, PAD)
+    packed, cu_real, cu_pad, status = thd.pack(dev_i64(rows), PAD, EOD, align, capacity, max_docs, PAD)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(packed.cpu().numpy(), want[0])
+    assert np.array_equal(cu_real.cpu().numpy(), want[1])
+    assert np.array_equal(cu_pad.cpu().numpy(), want[2])
