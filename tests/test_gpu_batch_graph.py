@@ -244,3 +244,78 @@ def test_graph_capture_replays_build_swaps_and_roll(thd):
     assert np.array_equal(a.cpu().numpy(), want_a)
     for k in range(2):
         assert np.array_equal(shifted[k].cpu().numpy(), want_s[k])
+
+
+def test_graph_capture_of_the_whole_chain_from_token_rows(thd):
+    # Pack -> route build -> zigzag roll -> multi-key swap captured in one
+    # HIP graph (every shape fixed on the host by the token budget); replays
+    # with eager work in between must match the oracle, and so must a replay
+    # after new token rows are written into the captured input.
+    import torch
+    cp, batch, seq, max_docs = 4, 6, 1500, 120
+    align = 2 * cp * 2
+    capacity = ((batch * seq) // align + max_docs + 1) * align
+    n_slots = max_docs + 1
+    rows_a = W.token_rows(600, batch, seq, 0, 1, 0.004, 300, 0.0)
+    rows_b = W.token_rows(601, batch, seq, 0, 1, 0.01, 100, 0.0)
+    tokens = dev_i64(rows_a)
+    nbytes = thd.thd_pack_workspace_bytes(batch, seq)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    packed = torch.empty(capacity, dtype=torch.int64, device="cuda")
+    cu_real = torch.empty(max_docs + 2, dtype=torch.int32, device="cuda")
+    cu_pad = torch.empty(max_docs + 2, dtype=torch.int32, device="cuda")
+    pstatus = torch.empty(1, dtype=torch.int32, device="cuda")
+    rstatus = torch.empty(1, dtype=torch.int32, device="cuda")
+    route = thd.Route(n_slots, cp, capacity)
+    shifted = torch.empty((2, capacity), dtype=torch.int64, device="cuda")
+    mask = torch.empty((3, capacity), dtype=torch.uint8, device="cuda")
+    pos = torch.arange(capacity, dtype=torch.int64, device="cuda")
+    zig_tokens, zig_pos = torch.empty_like(packed), torch.empty_like(pos)
+
+    def step(stream):
+        thd.thd_pack(tokens, batch, seq, 0, 1, align, capacity, max_docs, 0, ws, nbytes, packed, cu_real, cu_pad,
+                     pstatus, stream)
+        thd.thd_build_route(route.handle, cu_pad, n_slots, cp, capacity, stream)
+        thd.thd_roll_labels_zigzag(route.handle, packed, cu_pad, cu_real, n_slots, capacity, 2, -1, shifted, mask,
+                                   rstatus, stream)
+        thd.thd_swap_batch(route.handle, thd.C2Z, [packed, pos], [zig_tokens, zig_pos], [8, 8], capacity, stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+    def check(rows):
+        p, cr, cpd = O.pack_batch(rows, 0, 1, align, capacity, max_docs, 0)
+        assert int(pstatus.item()) == 0 and int(rstatus.item()) == 0 and route.status() == 0
+        assert np.array_equal(packed.cpu().numpy(), p)
+        assert np.array_equal(cu_pad.cpu().numpy(), cpd) and np.array_equal(cu_real.cpu().numpy(), cr)
+        ws_, wm_ = O.roll_labels(p, cpd, cr, capacity, 2, -1)
+        for k in range(2):
+            assert np.array_equal(shifted[k].cpu().numpy(), O.swap_rows(ws_[k], cpd, cp, capacity, "c2z"))
+        for k in range(3):
+            assert np.array_equal(mask[k].cpu().numpy(), O.swap_rows(wm_[k], cpd, cp, capacity, "c2z"))
+        assert np.array_equal(zig_tokens.cpu().numpy(), O.swap_rows(p, cpd, cp, capacity, "c2z"))
+        assert np.array_equal(zig_pos.cpu().numpy(), O.layout_tokens(cpd, cp, capacity, O.ZIGZAG))
+
+    for rep in range(3):
+        for t in (packed, shifted, zig_tokens, zig_pos):
+            t.fill_(-3)
+        mask.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("chain graph replay", rep)
+        check(rows_a)
+        _ = (pos.float().sum() + 1).item()           # eager work between replays
+    tokens.copy_(dev_i64(rows_b))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    check(rows_b)
