@@ -122,6 +122,9 @@ def test_random_swap_parity(thd, case):
     (4096, 0, 1, 128, 64, 4096), (8192, 0, 1, 512, 3, 8192), (0, 11, 1, 0, 1 << 30, 8192), (0, 0, 1, 0, 7, 48),
     # rows cut into slices (tile_bytes below the row size)
     (4096, 0, 1, 128, 1, 8192), (2048, 0, 1, 128, 64, 8192), (3000, 9, 0, 256, 1, 8208), (16, 0, 1, 128, 5, 4096),
+    # the built-in shape on row sizes between and beyond the measured ones
+    (0, 0, 1, 0, 0, 6144), (0, 0, 1, 0, 0, 4112), (0, 0, 1, 0, 0, 12288), (0, 0, 1, 0, 0, 65536),
+    (0, 0, 1, 0, 0, 10000),
 ])
 def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt, block, order, rb):
     import torch
