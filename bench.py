@@ -36,7 +36,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="gdn128k")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
