@@ -40,6 +40,7 @@ constexpr int kChunk = 1024;          // tokens per chunk (one workgroup)
 constexpr int kChunkThreads = 256;
 constexpr int kPer = kChunk / kChunkThreads;  // consecutive tokens per thread
 constexpr int kScanThreads = 1024;
+constexpr int kFusedChunks = 256;  // up to this many chunks (one scan pass) each write workgroup runs the scan itself
 
 // Length of a document of `len` tokens once padded to a multiple of align.
 __device__ __forceinline__ int64_t padded_len(int32_t len, int32_t align) {
@@ -98,21 +99,34 @@ __global__ __launch_bounds__(kChunkThreads) void pack_chunks_kernel(const int64_
   }
 }
 
-// Scan pass: one workgroup over all chunks in batch order.  Row boundaries
-// are handled without segmented scans: a position p of row b is keyed
-// b * (seq + 1) + p, so a running maximum never carries a value from an
-// earlier row past the row's own base key.
-__global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int32_t n_total, int32_t seq, int32_t n_ch,
-                                                                 int32_t align, int32_t max_docs, int32_t capacity,
-                                                                 PackWs ws, int32_t* __restrict__ cu_real,
-                                                                 int32_t* __restrict__ cu_pad,
-                                                                 int32_t* __restrict__ status) {
-  __shared__ int64_t s_scan[3 * (kScanThreads / 64 + 1)];
+// What the scan over all chunks gives one chunk and its row.
+struct ChunkPlace {
+  int32_t prev;        // end of the last document of the row closed before the chunk
+  int32_t valid_end;   // the row's valid end
+  int64_t doc_base;    // index of the first document that ends in or after the chunk
+  int64_t pack_base;   // packed position of the document holding the chunk's first token
+  int64_t real_off;    // valid tokens of the earlier rows
+};
+
+struct PackTotals {
+  int64_t docs, padded, real;
+};
+
+// Scan over all chunks in batch order, by one workgroup of kThreads.  Row
+// boundaries are handled without segmented scans: a position p of row b is
+// keyed b * (seq + 1) + p, so a running maximum never carries a value from an
+// earlier row past the row's own base key.  With `store`, every chunk's and
+// row's results go to the workspace; with want >= 0, those of chunk `want`
+// and its row go to *place (LDS).  Every thread gets the totals.
+template <int kThreads>
+__device__ PackTotals scan_chunks(int32_t n_total, int32_t seq, int32_t n_ch, int32_t align, const PackWs& ws,
+                                  int64_t* s_scan, bool store, int32_t want, ChunkPlace* place) {
   const int tid = threadIdx.x;
   const int64_t stride = static_cast<int64_t>(seq) + 1;
+  const int32_t want_row = want >= 0 ? want / n_ch : -1;
   int64_t carry_eod = 0, carry_np = 0;            // running maxima of the keyed positions
   int64_t carry_d = 0, carry_p = 0, carry_r = 0;  // running sums: documents, padded, real
-  for (int32_t base = 0; base < n_total; base += kScanThreads) {
+  for (int32_t base = 0; base < n_total; base += kThreads) {
     const int32_t c = base + tid;
     const bool in = c < n_total;
     const int32_t b = in ? c / n_ch : 0;
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int32_t n_total
     const int64_t key0 = b * stride;
     const int64_t mv[2] = {in ? key0 + le : 0, in ? key0 + lnp : 0};
     int64_t mx[2], mt[2];
-    block_exclusive_multi<kScanThreads, 2, true>(mv, 0, s_scan, mx, mt);
+    block_exclusive_multi<kThreads, 2, true>(mv, 0, s_scan, mx, mt);
     const int64_t ex_eod = max(mx[0], carry_eod), ex_np = max(mx[1], carry_np);
     carry_eod = max(carry_eod, mt[0]);
     carry_np = max(carry_np, mt[1]);
@@ -137,48 +151,83 @@ __global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int32_t n_total
     // end of the last document closed before this chunk (row coordinates)
     const int32_t prev_end = static_cast<int32_t>(max(ex_eod, key0) - key0);
     int64_t d = ne, p = 0, r = 0;
+    int32_t valid_end = 0;
     if (ne) p = padded_len(fe - prev_end, align) + ps;
     if (row_last) {
-      const int32_t valid_end = static_cast<int32_t>(max(max(ex_np, mv[1]), key0) - key0);
+      valid_end = static_cast<int32_t>(max(max(ex_np, mv[1]), key0) - key0);
       const int32_t last_eod = static_cast<int32_t>(max(max(ex_eod, mv[0]), key0) - key0);
       if (valid_end > last_eod) {  // the document after the row's last EOD
         d += 1;
         p += padded_len(valid_end - last_eod, align);
       }
       r = valid_end;
-      ws.row_valid[b] = valid_end;
     }
     const int64_t sv[3] = {d, p, r};
     int64_t sx[3], st[3];
-    block_exclusive_multi<kScanThreads, 3, false>(sv, 0, s_scan, sx, st);
+    block_exclusive_multi<kThreads, 3, false>(sv, 0, s_scan, sx, st);
     if (in) {
-      ws.ch_prev[c] = prev_end;
-      ws.ch_doc_base[c] = carry_d + sx[0];
-      ws.ch_pack_base[c] = carry_p + sx[1];
-      if (row_last) ws.row_real_off[b] = carry_r + sx[2];  // real tokens of the earlier rows
+      if (store) {
+        ws.ch_prev[c] = prev_end;
+        ws.ch_doc_base[c] = carry_d + sx[0];
+        ws.ch_pack_base[c] = carry_p + sx[1];
+        if (row_last) {
+          ws.row_valid[b] = valid_end;
+          ws.row_real_off[b] = carry_r + sx[2];  // real tokens of the earlier rows
+        }
+      }
+      if (c == want) {
+        place->prev = prev_end;
+        place->doc_base = carry_d + sx[0];
+        place->pack_base = carry_p + sx[1];
+      }
+      if (row_last && b == want_row) {
+        place->valid_end = valid_end;
+        place->real_off = carry_r + sx[2];
+      }
     }
     carry_d += st[0];
     carry_p += st[1];
     carry_r += st[2];
   }
-  const int64_t docs = carry_d, padded = carry_p, real = carry_r;
-  const int32_t code = docs > max_docs ? THD_ERR_PACK_DOCS : (padded > capacity ? THD_ERR_PACK_CAPACITY : THD_OK);
+  return PackTotals{carry_d, carry_p, carry_r};
+}
+
+// Status, header and the boundary lists' tail (the trailing pad slot, which
+// ends at the budget with no real tokens, and the empty slots), by one
+// workgroup.  Returns the status.
+template <int kThreads>
+__device__ int32_t pack_finish(const PackTotals& t, int32_t max_docs, int32_t capacity, const PackWs& ws,
+                               int32_t* cu_real, int32_t* cu_pad, int32_t* status) {
+  const int tid = threadIdx.x;
+  const int32_t code =
+      t.docs > max_docs ? THD_ERR_PACK_DOCS : (t.padded > capacity ? THD_ERR_PACK_CAPACITY : THD_OK);
   if (tid == 0) {
     ws.hdr[0] = code;
-    ws.hdr[1] = static_cast<int32_t>(min(docs, static_cast<int64_t>(INT32_MAX)));
-    ws.hdr[2] = static_cast<int32_t>(min(padded, static_cast<int64_t>(INT32_MAX)));
+    ws.hdr[1] = static_cast<int32_t>(min(t.docs, static_cast<int64_t>(INT32_MAX)));
+    ws.hdr[2] = static_cast<int32_t>(min(t.padded, static_cast<int64_t>(INT32_MAX)));
     if (status) *status = code;
   }
-  if (code != THD_OK) return;
+  if (code != THD_OK) return code;
   if (tid == 0) {
     cu_real[0] = 0;
     cu_pad[0] = 0;
   }
-  // trailing pad slot (ends at the budget, no real tokens) and empty slots
-  for (int64_t k = docs + 1 + tid; k <= static_cast<int64_t>(max_docs) + 1; k += kScanThreads) {
-    cu_real[k] = static_cast<int32_t>(real);
+  for (int64_t k = t.docs + 1 + tid; k <= static_cast<int64_t>(max_docs) + 1; k += kThreads) {
+    cu_real[k] = static_cast<int32_t>(t.real);
     cu_pad[k] = capacity;
   }
+  return code;
+}
+
+// Scan pass for batches of many chunks: one workgroup.
+__global__ __launch_bounds__(kScanThreads) void pack_scan_kernel(int32_t n_total, int32_t seq, int32_t n_ch,
+                                                                 int32_t align, int32_t max_docs, int32_t capacity,
+                                                                 PackWs ws, int32_t* __restrict__ cu_real,
+                                                                 int32_t* __restrict__ cu_pad,
+                                                                 int32_t* __restrict__ status) {
+  __shared__ int64_t s_scan[3 * (kScanThreads / 64 + 1)];
+  const PackTotals t = scan_chunks<kScanThreads>(n_total, seq, n_ch, align, ws, s_scan, true, -1, nullptr);
+  pack_finish<kScanThreads>(t, max_docs, capacity, ws, cu_real, cu_pad, status);
 }
 
 struct PadRun {
@@ -187,22 +236,47 @@ struct PadRun {
 };
 
 // Write pass: one workgroup per chunk, then every workgroup helps fill the
-// budget's tail.
+// budget's tail.  kFused (batches of at most kFusedChunks chunks): every
+// workgroup first runs the scan over all chunks itself, keeping only its own
+// chunk's results, and workgroup 0 writes the status and the lists' tail, so
+// the separate scan launch is not needed.
+template <bool kFused>
 __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t* __restrict__ tokens, int32_t seq,
                                                                    int32_t n_ch, int32_t n_chunks, int64_t eod_id,
                                                                    int32_t align, int64_t pad_value,
                                                                    int32_t capacity, int32_t max_docs, PackWs ws,
                                                                    int64_t* __restrict__ packed,
                                                                    int32_t* __restrict__ cu_real,
-                                                                   int32_t* __restrict__ cu_pad) {
+                                                                   int32_t* __restrict__ cu_pad,
+                                                                   int32_t* __restrict__ status) {
   __shared__ int64_t s_scan[3 * (kChunkThreads / 64 + 1)];
   __shared__ PadRun s_pads[kChunk];
-  if (ws.hdr[0] != THD_OK) return;  // over budget: nothing is written
+  __shared__ ChunkPlace s_place;
   const int tid = threadIdx.x;
   const int32_t c = blockIdx.x;
+  int64_t used;
+  if constexpr (kFused) {
+    const PackTotals t =
+        scan_chunks<kChunkThreads>(n_chunks, seq, n_ch, align, ws, s_scan, false, c < n_chunks ? c : -1, &s_place);
+    int32_t code;
+    if (c == 0) code = pack_finish<kChunkThreads>(t, max_docs, capacity, ws, cu_real, cu_pad, status);
+    else code = t.docs > max_docs || t.padded > capacity ? THD_ERR_PACK_DOCS : THD_OK;
+    if (code != THD_OK) return;  // over budget: nothing is written
+    used = t.padded;
+    __syncthreads();  // s_place is complete
+  } else {
+    if (ws.hdr[0] != THD_OK) return;  // over budget: nothing is written
+    used = ws.hdr[2];
+    if (tid == 0 && c < n_chunks) {
+      const int32_t b = c / n_ch;
+      s_place = ChunkPlace{ws.ch_prev[c], ws.row_valid[b], ws.ch_doc_base[c], ws.ch_pack_base[c],
+                           ws.row_real_off[b]};
+    }
+    __syncthreads();
+  }
   if (c < n_chunks) {
     const int32_t b = c / n_ch;
-    const int32_t valid_end = ws.row_valid[b];
+    const int32_t valid_end = s_place.valid_end;
     const int32_t chunk_start = (c - b * n_ch) * kChunk;
     const int32_t s0 = chunk_start + tid * kPer;
     const int64_t* row = tokens + static_cast<int64_t>(b) * seq;
@@ -220,7 +294,7 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
       const int64_t mv[1] = {le};
       int64_t mx[1], mt[1];
       block_exclusive_multi<kChunkThreads, 1, true>(mv, 0, s_scan, mx, mt);
-      const int32_t start0 = max(static_cast<int32_t>(mx[0]), ws.ch_prev[c]);
+      const int32_t start0 = max(static_cast<int32_t>(mx[0]), s_place.prev);
       int64_t plen_sum = 0, pad_sum = 0, n_end = 0;
       int32_t st = start0;
 #pragma unroll
@@ -242,9 +316,9 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
       const int32_t end_off = static_cast<int32_t>(sx[2]);
       const int32_t end_total = static_cast<int32_t>(min(stot[2], static_cast<int64_t>(kChunk)));
 
-      const int64_t real_off = ws.row_real_off[b];
-      int64_t pos = ws.ch_pack_base[c] + pl_off;  // packed start of the current document
-      int64_t k = ws.ch_doc_base[c] + end_off;    // its index
+      const int64_t real_off = s_place.real_off;
+      int64_t pos = s_place.pack_base + pl_off;  // packed start of the current document
+      int64_t k = s_place.doc_base + end_off;    // its index
       int64_t pads_seen = pad_off;
       int32_t slot = end_off;
       st = start0;
@@ -285,7 +359,6 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
       }
     }
   }
-  const int64_t used = ws.hdr[2];
   for (int64_t i = used + static_cast<int64_t>(blockIdx.x) * kChunkThreads + tid; i < capacity;
        i += static_cast<int64_t>(gridDim.x) * kChunkThreads)
     packed[i] = pad_value;
@@ -311,14 +384,21 @@ hipError_t launch_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_
     if (e != hipSuccess) return e;
   }
   const int32_t n_ch_arg = n_ch > 0 ? n_ch : 1;
-  hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, static_cast<int32_t>(n_chunks), seq,
-                     n_ch_arg, align, max_docs, capacity, ws, cu_real, cu_pad, status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t grid = n_chunks > 0 ? n_chunks : 1;
-  hipLaunchKernelGGL(pack_write_kernel, dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), 0, stream, tokens,
-                     seq, n_ch_arg, static_cast<int32_t>(n_chunks), eod_id, align, pad_value, capacity, max_docs, ws,
-                     packed, cu_real, cu_pad);
+#define THD_PACK_WRITE(F)                                                                                           \
+  hipLaunchKernelGGL((pack_write_kernel<F>), dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), 0, stream,     \
+                     tokens, seq, n_ch_arg, static_cast<int32_t>(n_chunks), eod_id, align, pad_value, capacity,      \
+                     max_docs, ws, packed, cu_real, cu_pad, status)
+  if (n_chunks <= kFusedChunks) {
+    THD_PACK_WRITE(true);
+  } else {
+    hipLaunchKernelGGL(pack_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, static_cast<int32_t>(n_chunks), seq,
+                       n_ch_arg, align, max_docs, capacity, ws, cu_real, cu_pad, status);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    THD_PACK_WRITE(false);
+  }
+#undef THD_PACK_WRITE
   return hipGetLastError();
 }
 
