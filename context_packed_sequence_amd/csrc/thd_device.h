@@ -104,7 +104,7 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
 struct FastDiv {
   uint32_t m;
   int l;
-  __device__ static FastDiv make(int32_t d) {
+  __host__ __device__ static FastDiv make(int32_t d) {
     FastDiv f{0, 0};
     while ((1u << f.l) < static_cast<uint32_t>(d)) ++f.l;
     const uint64_t num = (uint64_t{1} << 32) * ((uint64_t{1} << f.l) - static_cast<uint64_t>(d));

@@ -80,7 +80,8 @@ __device__ __forceinline__ Cut cut_segment(const Segment& s, int32_t share, cons
 // mostly hit the same few (source, destination) entries and atomics from many
 // lanes to one LDS address serialise.  The copies are summed afterwards.
 constexpr int kSplitEntries = 1024;  // cp * cp * copies stays within this
-__host__ __device__ inline int split_copies(int32_t cp) {
+__host__ __device__ inline int split_copies(int32_t cp, int32_t n_slots) {
+  if (2LL * cp * n_slots <= 1024) return 1;  // one pass over the segments: few atomics to spread
   const int64_t sq = static_cast<int64_t>(cp) * cp;
   if (sq >= kSplitEntries) return 1;
   const int c = static_cast<int>(kSplitEntries / sq);
@@ -88,7 +89,7 @@ __host__ __device__ inline int split_copies(int32_t cp) {
 }
 
 // The build kernel keeps the compacted documents and the split matrix (in
-// split_copies(cp) copies) in LDS when they fit in kBuildLdsBytes; otherwise
+// split_copies(cp, n_slots) copies) in LDS when they fit in kBuildLdsBytes; otherwise
 // it uses the route's global scratch and global atomics (same steps, slower).
 constexpr int kBuildLdsBytes = 60 * 1024;
 
@@ -128,18 +129,18 @@ __device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, in
 template <bool kLds, bool kFused>
 __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
                                                                     int32_t cp, int32_t total, RouteDev ws,
-                                                                    int32_t lds_run_cap) {
+                                                                    int32_t lds_run_cap, FastDiv div_share,
+                                                                    FastDiv div_two_cp) {
   // kLds: docs[3 * n_slots], split[copies * cp * cp]; kFused adds, 8-byte
   // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
   extern __shared__ int32_t s_dyn[];
   __shared__ int s_wave[kBuildWaves + 1];
   __shared__ int s_sev;
-  __shared__ FastDiv s_div[3];  // by share, 2 * n_docs, 2 * cp
   const int tid = threadIdx.x;
   const bool writer = !kFused || blockIdx.x == 0;  // the workgroup that writes the route out
   const int32_t cap = kLds ? n_slots : ws.docs_cap;
   const int32_t cp2 = cp * cp;
-  const int copies = kLds ? split_copies(cp) : 1;
+  const int copies = kLds ? split_copies(cp, n_slots) : 1;
   int32_t* docs = kLds ? s_dyn : ws.docs;
   int32_t* split = kLds ? s_dyn + 3 * n_slots : ws.split;
   int32_t* my_split = split + (threadIdx.x & 63) % copies * cp2;  // this lane's copy
@@ -182,11 +183,6 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     n_docs += sum;
   }
   if (sev) atomicMax(&s_sev, sev);
-  if (tid == 0) {
-    s_div[0] = FastDiv::make(total / cp > 0 ? total / cp : 1);
-    s_div[1] = FastDiv::make(n_docs > 0 ? 2 * n_docs : 1);
-    s_div[2] = FastDiv::make(two_cp);
-  }
   if constexpr (!kLds) __threadfence();  // global path: zeroed split and document list are complete
   __syncthreads();                       // publishes the document list to the whole workgroup
   if (s_sev) {
@@ -207,9 +203,14 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   const int32_t n_seg = two_cp * n_docs;
   const int32_t two_n = 2 * n_docs;
   bool overflow = false;
-  // the loop below divides by these three on every segment (set up once by
-  // thread 0 before the barrier that publishes the documents)
-  const FastDiv div_share = s_div[0], div_two_n = s_div[1], div_two_cp = s_div[2];
+  // segment j of the zigzag-row order is (rank r, position rem in the rank's
+  // 2 * n_docs chunks); j grows by kBuildThreads per pass, so r and rem are
+  // stepped instead of divided again (the other divisions, by share and by
+  // 2 * cp, use the host's multiply-high constants)
+  const int32_t step_r = n_seg > 0 ? kBuildThreads / two_n : 0;
+  const int32_t step_rem = n_seg > 0 ? kBuildThreads - step_r * two_n : 0;
+  int32_t r_j = n_seg > 0 ? tid / two_n : 0;
+  int32_t rem_j = n_seg > 0 ? tid - r_j * two_n : 0;
 
   // ---- 3+4. runs in zigzag-row order (with the split matrix) and in token
   //           order.  Thread j looks at segment j of each order, counts the
@@ -218,13 +219,20 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   int32_t n_src = 0, n_dst = 0;
   for (int32_t base = 0; base < n_seg; base += kBuildThreads) {
     const int32_t j = base + tid;
+    const int32_t r = r_j, rem = rem_j;  // j = r * two_n + rem
+    if (base + kBuildThreads < n_seg) {
+      r_j += step_r;
+      rem_j += step_rem;
+      if (rem_j >= two_n) {
+        rem_j -= two_n;
+        ++r_j;
+      }
+    }
     int32_t merge_s = 0, merge_t = 0;
     Segment ss{}, st{};
     Cut cs{0, 0, 0}, ct{0, 0, 0};
     if (j < n_seg) {
       // zigzag-row order: rank-major, then document, then front/back chunk
-      const int32_t r = div_two_n(j);
-      const int32_t rem = j - r * two_n;
       const int32_t k = rem >> 1;
       const bool back = rem & 1;
       const Doc dk = load_doc(docs, cap, k);
@@ -414,7 +422,7 @@ __global__ __launch_bounds__(kIndexThreads) void route_index_kernel(RouteDev ws,
 // Dynamic LDS of the build kernel: documents and split copies (int32), and,
 // fused, the runs of both orders (8-byte aligned).
 int64_t build_lds_bytes(int32_t n_slots, int32_t cp, bool fused) {
-  const int64_t words = 3LL * n_slots + static_cast<int64_t>(split_copies(cp)) * cp * cp;
+  const int64_t words = 3LL * n_slots + static_cast<int64_t>(split_copies(cp, n_slots)) * cp * cp;
   if (!fused) return 4 * words;
   return 4 * ((words + 1) & ~1LL) + 16 * (2LL * cp * n_slots + cp);
 }
@@ -427,19 +435,22 @@ bool route_build_fused(int32_t n_slots, int32_t cp) {
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total, const RouteDev& ws,
                               hipStream_t stream) {
   const int64_t lds = build_lds_bytes(n_slots, cp, false);
+  const FastDiv div_share = FastDiv::make(total / cp > 0 ? total / cp : 1);
+  const FastDiv div_two_cp = FastDiv::make(2 * cp);
   if (route_build_fused(n_slots, cp)) {
     const int32_t run_cap = 2 * cp * n_slots + cp;
     const int64_t lds_fused = build_lds_bytes(n_slots, cp, true);
     const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
     const int32_t grid = n_blocks > 0 ? (n_blocks + kDirPerFusedGroup - 1) / kDirPerFusedGroup : 1;
     hipLaunchKernelGGL((route_build_kernel<true, true>), dim3(grid), dim3(kBuildThreads),
-                       static_cast<size_t>(lds_fused), stream, cu, n_slots, cp, total, ws, run_cap);
+                       static_cast<size_t>(lds_fused), stream, cu, n_slots, cp, total, ws, run_cap, div_share,
+                       div_two_cp);
   } else if (lds <= kBuildLdsBytes) {
     hipLaunchKernelGGL((route_build_kernel<true, false>), dim3(1), dim3(kBuildThreads), static_cast<size_t>(lds),
-                       stream, cu, n_slots, cp, total, ws, 0);
+                       stream, cu, n_slots, cp, total, ws, 0, div_share, div_two_cp);
   } else {
     hipLaunchKernelGGL((route_build_kernel<false, false>), dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp,
-                       total, ws, 0);
+                       total, ws, 0, div_share, div_two_cp);
   }
   return hipGetLastError();
 }
