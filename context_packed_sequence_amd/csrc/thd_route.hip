@@ -6,8 +6,9 @@
 // contiguous layout, two per document per rank for the zigzag layout -- so the
 // whole exchange is an intersection of intervals instead of per-token index
 // tensors.  The pages do this with Python integers on the host after one
-// device-to-host copy of the boundaries; here one workgroup does it on the
-// device, so the host never waits.
+// device-to-host copy of the boundaries; here it runs on the device (one
+// workgroup, or every workgroup of one launch redundantly when the result
+// fits in LDS), so the host never waits.
 //
 // Layout facts used below ("Packed Sequence 与上下文并行" §2.4, §2.5, §3.5):
 //  * a padded document k of length L_k starting at token a_k is cut into 2*cp
@@ -89,8 +90,9 @@ __host__ __device__ inline int split_copies(int32_t cp, int32_t n_slots) {
 }
 
 // The build kernel keeps the compacted documents and the split matrix (in
-// split_copies(cp, n_slots) copies) in LDS when they fit in kBuildLdsBytes; otherwise
-// it uses the route's global scratch and global atomics (same steps, slower).
+// split_copies(cp, n_slots) copies) in LDS when they fit in kBuildLdsBytes;
+// otherwise it uses the route's global scratch and global atomics (same
+// steps, slower).
 constexpr int kBuildLdsBytes = 60 * 1024;
 
 // Fused build: when the runs of both orders fit in LDS as well, every

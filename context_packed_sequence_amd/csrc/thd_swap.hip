@@ -7,11 +7,12 @@
 //
 // The route is a list of runs sorted by output row; inside a run both the
 // input rows and the output rows are consecutive, so a run is one contiguous
-// byte range on each side.  The output rows are cut into tiles of whole rows
-// (about one row, or 4 KiB of small rows, per workgroup); the route's
-// directory entry for the tile's first row gives the input row, the end of its
-// run and the run index in one load.  A workgroup walks the runs that overlap
-// its tile (almost always one) and streams each piece as a flat copy:
+// byte range on each side.  The output rows are cut into tiles of about
+// 4 KiB per workgroup (whole rows, one row, or a slice of one long row); the
+// route's directory entry for the tile's first row gives the input row, the
+// end of its run, the run index and the run starts inside its 16-row block in
+// one load.  A workgroup walks the runs that overlap its tile (almost always
+// one) and streams each piece as a flat copy:
 // consecutive lanes touch consecutive 16-byte vectors, so every wave-wide load
 // and store is a fully coalesced 1 KiB access.  Run data is uniform across the
 // workgroup and is read through scalar loads.
