@@ -93,7 +93,7 @@ __host__ __device__ inline int split_copies(int32_t cp, int32_t n_slots) {
 // split_copies(cp, n_slots) copies) in LDS when they fit in kBuildLdsBytes;
 // otherwise it uses the route's global scratch and global atomics (same
 // steps, slower).
-constexpr int kBuildLdsBytes = 60 * 1024;
+constexpr int kBuildLdsBytes = 150 * 1024;  // of the 160 KiB a workgroup may hold on MI355X
 
 // Fused build: when the runs of both orders fit in LDS as well, every
 // workgroup of one launch builds the whole route in its own LDS (the work is
