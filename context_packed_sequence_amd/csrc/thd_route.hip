@@ -101,7 +101,7 @@ constexpr int kBuildLdsBytes = 150 * 1024;  // of the 160 KiB a workgroup may ho
 // it out, and each workgroup then writes its share of the directory from its
 // LDS copy.  One launch instead of build + directory, and no workgroup ever
 // waits for another.
-constexpr int kFusedMaxSegments = 4096;
+constexpr int kFusedMaxSegments = 16384;
 constexpr int kDirPerFusedGroup = 1024;  // directory rows per workgroup and direction
 
 // Largest i in [lo, hi) with runs[i].out <= row, given runs[lo].out <= row.
