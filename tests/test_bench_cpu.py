@@ -1,0 +1,27 @@
+"""bench.py contract checks that need no GPU."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    # one GPU only: the cross-rank exchange is emulated on one device
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+
+
+def test_step_bytes_counts_every_swap_and_the_roll():
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    w = workloads.make("full")
+    swap, roll, total = bench.step_bytes(w, w.layers)
+    assert swap == 2 * w.total * w.row_bytes
+    j = w.max_shift
+    assert roll == w.total * (8 + 8 * j + (j + 1))     # ids in; J shifted streams and J + 1 masks out
+    assert total == 2 * w.layers * swap + roll
