@@ -88,6 +88,23 @@ def _median_event_ms(torch, stream, fn, reps):
     return ts[len(ts) // 2]
 
 
+def _capture(torch, stream, launch_on):
+    """A HIP graph of launch_on(stream handle), after one eager run of it on a side stream."""
+    side = torch.cuda.Stream(device=stream.device)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch_on(side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch_on(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    return graph
+
+
 def measure_next(thd, torch, workloads, w, route, x, stream, step_on, reps=20):
     """The widened rows on the same batch: one-launch multi-key slice, roll
     written in zigzag order, device packing, and a graph-captured step."""
@@ -107,10 +124,17 @@ def measure_next(thd, torch, workloads, w, route, x, stream, step_on, reps=20):
         for k, o, r in zip(keys, outs, rbs):
             thd.thd_swap(route.handle, thd.C2Z, k, o, T, r, sh)
     t_sep = _median_event_ms(torch, stream, separate, reps)
+
+    def separate_on(s):
+        for k, o, r in zip(keys, outs, rbs):
+            thd.thd_swap(route.handle, thd.C2Z, k, o, T, r, s)
+    g_sep = _capture(torch, stream, separate_on)
+    t_sep_graph = _median_event_ms(torch, stream, g_sep.replay, reps)
     moved = 2 * T * sum(rbs)
     out["multi_key_swap"] = {"keys": "3 x int64 + 2 x uint8 per token", "us": round(t_batch * 1e3, 2),
                              "gbps": round(moved / (t_batch * 1e-3) / 1e9, 1),
-                             "five_thd_swap_calls_us": round(t_sep * 1e3, 2)}
+                             "five_thd_swap_calls_us": round(t_sep * 1e3, 2),
+                             "five_thd_swap_calls_graph_us": round(t_sep_graph * 1e3, 2)}
 
     # the tensors of one gated-delta-net layer (q, k, v with the activation's
     # row shape, then the decay gate g in fp32 and beta in bf16 per head)
@@ -176,17 +200,7 @@ def measure_next(thd, torch, workloads, w, route, x, stream, step_on, reps=20):
     out["pack"] = {"rows": f"[{batch},{seq}] int64", "capacity": capacity, "us": round(t_pack * 1e3, 2),
                    "gbps": round(pack_bytes / (t_pack * 1e-3) / 1e9, 1)}
 
-    side = torch.cuda.Stream(device=dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step_on(side.cuda_stream)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step_on(torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
-    graph.replay()
+    graph = _capture(torch, stream, step_on)
     t_graph = _median_event_ms(torch, stream, graph.replay, reps)
     t_eager = _median_event_ms(torch, stream, lambda: step_on(sh), reps)
     out["graph_step_ms"] = round(t_graph, 4)
@@ -282,29 +296,25 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(events=None):
-        if events is not None:
-            e = [ev() for _ in range(2 + 4 * layers + 2)]
-            events.append(e)
+    def step(e=None):
+        # e: four timing events, recorded before the build, between the build
+        # and the swaps, after the last swap and after the roll.  The swaps of
+        # all layers run back to back with no event between them: an event
+        # between two kernels on this runtime costs a few microseconds of
+        # idle device time and would slow the step it measures.
+        if e is not None:
             e[0].record(stream)
         thd.thd_build_route(h, cu, n_slots, cp, total, s_handle)
-        if events is not None:
+        if e is not None:
             e[1].record(stream)
         for layer in range(layers):
-            if events is not None:
-                e[2 + 4 * layer].record(stream)
             thd.thd_swap(h, thd.Z2C, x, a, total, rb, s_handle)
-            if events is not None:
-                e[3 + 4 * layer].record(stream)
-                e[4 + 4 * layer].record(stream)
             thd.thd_swap(h, thd.C2Z, a, b, total, rb, s_handle)
-            if events is not None:
-                e[5 + 4 * layer].record(stream)
-        if events is not None:
-            e[-2].record(stream)
+        if e is not None:
+            e[2].record(stream)
         thd.thd_roll_labels(ids, cu, cu_real, n_slots, total, j, 0, shifted, mask, status, s_handle)
-        if events is not None:
-            e[-1].record(stream)
+        if e is not None:
+            e[3].record(stream)
 
     # correctness guard (not timed): one step, then the round trip must be exact
     step()
@@ -316,27 +326,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-kernel events on the launch stream
-    events = []
+    # timed region: K steps, four events per step on the launch stream
+    events = [[ev() for _ in range(4)] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for _ in range(args.steps):
-        step(events)
+    for e in events:
+        step(e)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = t_start.elapsed_time(t_end)
     ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
 
-    swap_ms, build_ms, roll_ms = [], [], []
-    for e in events:
-        build_ms.append(e[0].elapsed_time(e[1]))
-        for layer in range(layers):
-            swap_ms.append(e[2 + 4 * layer].elapsed_time(e[3 + 4 * layer]))
-            swap_ms.append(e[4 + 4 * layer].elapsed_time(e[5 + 4 * layer]))
-        roll_ms.append(e[-2].elapsed_time(e[-1]))
+    # average swap launch: the back-to-back swaps of each step over their count
+    build_ms = [e[0].elapsed_time(e[1]) for e in events]
+    swap_ms = [e[1].elapsed_time(e[2]) / (2 * layers) for e in events]
+    roll_ms = [e[2].elapsed_time(e[3]) for e in events]
     swap_avg_ms = float(np.mean(swap_ms))
     swap_bytes, roll_bytes, total_bytes = step_bytes(w, layers)
     swap_gbps = swap_bytes / (swap_avg_ms * 1e-3) / 1e9
@@ -367,6 +374,12 @@ def main():
     thd.thd_copy(x, a, nbytes, s_handle)
     copy_stream_ms = _median_event_ms(torch, stream, lambda: thd.thd_copy(x, a, nbytes, s_handle), 20)
     copy_gbps = swap_bytes / (copy_dtod_ms * 1e-3) / 1e9
+    # each direction alone, after the timed region
+    by_dir = {}
+    for d, fn in (("z2c", lambda: thd.thd_swap(h, thd.Z2C, x, a, total, rb, s_handle)),
+                  ("c2z", lambda: thd.thd_swap(h, thd.C2Z, a, b, total, rb, s_handle))):
+        fn()
+        by_dir[d] = round(_median_event_ms(torch, stream, fn, 20) * 1e3, 2)
     stream_copy_gbps = swap_bytes / (copy_stream_ms * 1e-3) / 1e9
 
     def step_on(s):
@@ -413,9 +426,7 @@ def main():
         "route_build_enqueue_us": round(float(np.median(enq)) * 1e6, 2),
         "roll_us": round(float(np.median(roll_ms)) * 1e3, 2),
         "host_syncs": host_syncs,
-        "swap_us_by_direction": {
-            d: {"median": round(float(np.median(v)) * 1e3, 2), "min": round(float(np.min(v)) * 1e3, 2)}
-            for d, v in (("z2c", swap_ms[0::2]), ("c2z", swap_ms[1::2]))},
+        "swap_us_by_direction": by_dir,
         "copy_ceiling_gbps": {"dtod_copy": round(copy_gbps, 1), "stream_copy": round(stream_copy_gbps, 1)},
         "roofline": {
             "bound": "hbm",
