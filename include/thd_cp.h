@@ -102,14 +102,19 @@ void thd_route_destroy(thd_route* route);
  * §2.1), so one build serves every layer, both directions and the recompute
  * replay of a micro-batch; rebuild it for the next micro-batch.
  *
- * One kernel with one workgroup validates the boundaries (codes
- * THD_ERR_CU_START .. THD_ERR_CU_DIVISIBLE, in that precedence), drops empty
- * slots, lays out the 2*cp zigzag segments of every document, cuts them at the
- * contiguous ranks' borders and writes the maximal runs (in zigzag-row order
- * and in token order) plus the cp x cp split matrix; a second, grid-wide
- * kernel writes, for every 16th output row of each direction, the input row
- * feeding it, the end of its run and the run's index.  Results and
- * the status word stay on the device.
+ * The build validates the boundaries (codes THD_ERR_CU_START ..
+ * THD_ERR_CU_DIVISIBLE, in that precedence), drops empty slots, lays out the
+ * 2*cp zigzag segments of every document, cuts them at the contiguous ranks'
+ * borders and writes the maximal runs (in zigzag-row order and in token
+ * order) plus the cp x cp split matrix, then a row directory: for every 16th
+ * output row of each direction, the input row feeding it, the end of its run,
+ * the run's index and which of the 16 rows start a run.  When 2*cp*n_slots
+ * <= 16384 and the route fits in 150 KiB of LDS this is one launch of
+ * ceil(total_tokens / 16384) workgroups, each building the route in its own
+ * LDS and writing its share of the directory; larger batches take one
+ * single-workgroup build launch (in LDS, or in the route's workspace when
+ * LDS is too small) and one grid-wide directory launch.  Results and the
+ * status word stay on the device.
  *
  * cp_size == 1: the route is the identity; nothing is launched and the
  * boundaries are not read (the swap short-circuits for one rank before any
