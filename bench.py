@@ -23,6 +23,7 @@ import argparse
 import json
 import os
 import platform
+import struct
 import sys
 import time
 
@@ -75,7 +76,8 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def _median_event_ms(torch, stream, fn, reps):
+def _event_samples(torch, stream, fn, reps):
+    """Device time of fn() in ms, one sample per call, from events on the launch stream."""
     evs = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -84,7 +86,11 @@ def _median_event_ms(torch, stream, fn, reps):
         b.record(stream)
         evs.append((a, b))
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def _median_event_ms(torch, stream, fn, reps):
+    ts = sorted(_event_samples(torch, stream, fn, reps))
     return ts[len(ts) // 2]
 
 
@@ -297,24 +303,20 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(e=None):
-        # e: four timing events, recorded before the build, between the build
-        # and the swaps, after the last swap and after the roll.  The swaps of
-        # all layers run back to back with no event between them: an event
-        # between two kernels on this runtime costs a few microseconds of
-        # idle device time and would slow the step it measures.
-        if e is not None:
-            e[0].record(stream)
+        # e: two timing events, recorded just before the first swap and just
+        # after the last.  The swaps of all layers run back to back with no
+        # event between them: an event between two kernels on this runtime
+        # leaves the device idle for a few microseconds and would slow the
+        # step it measures.
         thd.thd_build_route(h, cu, n_slots, cp, total, s_handle)
         if e is not None:
-            e[1].record(stream)
+            e[0].record(stream)
         for layer in range(layers):
             thd.thd_swap(h, thd.Z2C, x, a, total, rb, s_handle)
             thd.thd_swap(h, thd.C2Z, a, b, total, rb, s_handle)
         if e is not None:
-            e[2].record(stream)
+            e[1].record(stream)
         thd.thd_roll_labels(ids, cu, cu_real, n_slots, total, j, 0, shifted, mask, status, s_handle)
-        if e is not None:
-            e[3].record(stream)
 
     # correctness guard (not timed): one step, then the round trip must be exact
     step()
@@ -326,8 +328,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, four events per step on the launch stream
-    events = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    # timed region: K steps, two events per step on the launch stream
+    events = [[ev(), ev()] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -341,12 +343,15 @@ def main():
     ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
 
     # average swap launch: the back-to-back swaps of each step over their count
-    build_ms = [e[0].elapsed_time(e[1]) for e in events]
-    swap_ms = [e[1].elapsed_time(e[2]) / (2 * layers) for e in events]
-    roll_ms = [e[2].elapsed_time(e[3]) for e in events]
+    swap_ms = [e[0].elapsed_time(e[1]) / (2 * layers) for e in events]
     swap_avg_ms = float(np.mean(swap_ms))
     swap_bytes, roll_bytes, total_bytes = step_bytes(w, layers)
     swap_gbps = swap_bytes / (swap_avg_ms * 1e-3) / 1e9
+
+    # route build and roll device times: events around single launches, after the timed region
+    build_ms = _event_samples(torch, stream, lambda: thd.thd_build_route(h, cu, n_slots, cp, total, s_handle), 50)
+    roll_ms = _event_samples(torch, stream, lambda: thd.thd_roll_labels(ids, cu, cu_real, n_slots, total, j, 0,
+                                                                        shifted, mask, status, s_handle), 50)
 
     # route build: host enqueue time of the build call alone (device time from the events above)
     torch.cuda.synchronize()
@@ -374,6 +379,18 @@ def main():
     thd.thd_copy(x, a, nbytes, s_handle)
     copy_stream_ms = _median_event_ms(torch, stream, lambda: thd.thd_copy(x, a, nbytes, s_handle), 20)
     copy_gbps = swap_bytes / (copy_dtod_ms * 1e-3) / 1e9
+    # the two pure streams, each over the bytes one swap moves (2 x the
+    # activation): a swap or a copy mixes reads and writes on the same HBM
+    # channels and cannot move bytes faster than either pure stream
+    scratch = torch.empty(2 * nbytes, dtype=torch.uint8, device=dev)
+    hits = torch.zeros(1, dtype=torch.int32, device=dev)
+    thd.thd_write_stream(scratch, 2 * nbytes, 1, s_handle)
+    write_ms = _median_event_ms(torch, stream, lambda: thd.thd_write_stream(scratch, 2 * nbytes, 1, s_handle), 20)
+    key = struct.pack("<4I", 1, 2, 3, 4)  # never written: every written word repeats one value
+    thd.thd_read_stream(scratch, 2 * nbytes, key, hits, s_handle)
+    read_ms = _median_event_ms(torch, stream, lambda: thd.thd_read_stream(scratch, 2 * nbytes, key, hits, s_handle), 20)
+    assert int(hits.item()) == 0
+    del scratch, hits
     # each direction alone, after the timed region
     by_dir = {}
     for d, fn in (("z2c", lambda: thd.thd_swap(h, thd.Z2C, x, a, total, rb, s_handle)),
@@ -428,6 +445,8 @@ def main():
         "host_syncs": host_syncs,
         "swap_us_by_direction": by_dir,
         "copy_ceiling_gbps": {"dtod_copy": round(copy_gbps, 1), "stream_copy": round(stream_copy_gbps, 1)},
+        "stream_gbps": {"read_only": round(swap_bytes / (read_ms * 1e-3) / 1e9, 1),
+                        "write_only": round(swap_bytes / (write_ms * 1e-3) / 1e9, 1)},
         "roofline": {
             "bound": "hbm",
             "achieved": round(swap_gbps, 1),

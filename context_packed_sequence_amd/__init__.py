@@ -41,6 +41,8 @@ from .binding import (  # noqa: F401
     ThdError,
     thd_build_route,
     thd_copy,
+    thd_read_stream,
+    thd_write_stream,
     thd_pack,
     thd_pack_workspace_bytes,
     thd_roll_labels,

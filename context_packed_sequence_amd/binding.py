@@ -51,6 +51,7 @@ EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",
     "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_swap_tuning", "thd_strerror",
     "thd_swap_batch", "thd_roll_labels_zigzag", "thd_pack_workspace_bytes", "thd_pack", "thd_copy",
+    "thd_read_stream", "thd_write_stream",
 )
 
 
@@ -85,6 +86,8 @@ def _load() -> ctypes.CDLL:
                                                   c_p]),
         "thd_pack_workspace_bytes": (ctypes.c_int64, [c_i32, c_i32]),
         "thd_copy": (ctypes.c_int, [c_p, c_p, c_i64, c_p]),
+        "thd_read_stream": (ctypes.c_int, [c_p, c_i64, c_p, c_p, c_p]),
+        "thd_write_stream": (ctypes.c_int, [c_p, c_i64, ctypes.c_uint32, c_p]),
         "thd_pack": (ctypes.c_int, [c_p, c_i32, c_i32, c_i64, c_i64, c_i32, c_i64, c_i32, c_i64, c_p, c_i64, c_p,
                                     c_p, c_p, c_p, c_p]),
     }
@@ -194,6 +197,18 @@ def thd_pack(tokens, batch: int, seq: int, pad_id: int, eod_id: int, align: int,
 
 def thd_copy(x, out, nbytes: int, stream=None) -> int:
     return _check(_lib.thd_copy(_ptr(x), _ptr(out), nbytes, _stream(stream)), "thd_copy")
+
+
+def thd_read_stream(x, nbytes: int, key: bytes, count, stream=None) -> int:
+    """Add to count (device uint32) the number of 16-byte words of x equal to key (16 bytes)."""
+    if len(key) != 16:
+        raise ValueError("key must be 16 bytes")
+    k = ctypes.create_string_buffer(bytes(key), 16)
+    return _check(_lib.thd_read_stream(_ptr(x), nbytes, k, _ptr(count), _stream(stream)), "thd_read_stream")
+
+
+def thd_write_stream(out, nbytes: int, seed: int, stream=None) -> int:
+    return _check(_lib.thd_write_stream(_ptr(out), nbytes, seed & 0xFFFFFFFF, _stream(stream)), "thd_write_stream")
 
 
 def thd_route_status(route: int, stream=None) -> int:

@@ -28,7 +28,7 @@ LIB_NAME = "libthdcp.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["thd_route.hip", "thd_swap.hip", "thd_roll.hip", "thd_pack.hip", "thd_api.hip"]
+SOURCES = ["thd_route.hip", "thd_swap.hip", "thd_roll.hip", "thd_pack.hip", "thd_stream.hip", "thd_api.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -64,7 +64,7 @@ def _compile(src: str, asm: bool) -> str:
 def build(verbose: bool = False, asm: bool = False) -> str:
     """Compile every source and link libthdcp.so; return its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, asm), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -204,6 +204,26 @@ int thd_copy(const void* in, void* out, int64_t bytes, void* stream) {
   return THD_OK;
 }
 
+int thd_read_stream(const void* in, int64_t bytes, const void* key, uint32_t* count, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return THD_ERR_ARG;
+  if (bytes == 0) return THD_OK;
+  if (!in || !key || !count) return THD_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(in) & 15) || (reinterpret_cast<uintptr_t>(count) & 3)) return THD_ERR_ARG;
+  if (overlaps(in, bytes, count, 4)) return THD_ERR_ALIAS;
+  uint32_t k[4];
+  std::memcpy(k, key, sizeof(k));
+  if (thdcp::launch_read_stream(in, bytes, k, count, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
+  return THD_OK;
+}
+
+int thd_write_stream(void* out, int64_t bytes, uint32_t seed, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return THD_ERR_ARG;
+  if (bytes == 0) return THD_OK;
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 15)) return THD_ERR_ARG;
+  if (thdcp::launch_write_stream(out, bytes, seed, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
+  return THD_OK;
+}
+
 int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const int32_t* cu_seqlens, int32_t n_slots,
                     int64_t total_tokens, int32_t max_shift, int64_t fill, int64_t* shifted, uint8_t* mask,
                     int32_t* status, void* stream) {

@@ -81,6 +81,9 @@ struct SwapLaunch {
 
 // Plain streaming copy (thd_copy); cfg.block_threads and cfg.tile_order apply.
 hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunch& cfg, hipStream_t stream);
+hipError_t launch_read_stream(const void* in, int64_t bytes, const uint32_t key[4], uint32_t* count,
+                              hipStream_t stream);
+hipError_t launch_write_stream(void* out, int64_t bytes, uint32_t seed, hipStream_t stream);
 hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                        const void* in, void* out, int32_t total, int64_t row_bytes,
                        const SwapLaunch& cfg, hipStream_t stream);

@@ -322,6 +322,32 @@ int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontempo
  */
 int thd_copy(const void* in, void* out, int64_t bytes, void* stream);
 
+/*
+ * thd_read_stream / thd_write_stream -- the two streams any row permutation
+ * is made of, measured on their own: the swap reads each input byte once and
+ * writes each output byte once.  HBM carries reads and writes over the same
+ * channels, so a stream that mixes them (a copy, a swap) cannot move bytes
+ * faster than a pure read or a pure write stream; these two passes measure
+ * the pure streams.  Both use 16-byte non-temporal accesses, 128-thread
+ * workgroups and XCD-chunked tile order, in the shapes that streamed fastest
+ * on MI355X (4 KiB tiles for the read pass, 2 KiB for the write pass).
+ *
+ * thd_read_stream reads `bytes` bytes of `in` and adds to *count (device
+ * uint32, 4-byte aligned, cleared by the caller) the number of 16-byte words
+ * of `in` equal to the 16 bytes at `key` (host).  Only workgroups that find
+ * a match touch *count, so with rare matches nothing but reads reach HBM.
+ *
+ * thd_write_stream writes `bytes` bytes of `out`: 16-byte word w holds four
+ * copies of the 32-bit value (uint32)w ^ seed; nothing is read.
+ *
+ * `bytes` must be a non-negative multiple of 16 and `in` / `out` 16-byte
+ * aligned (THD_ERR_ARG otherwise, or for a null pointer with bytes > 0);
+ * `count` must not lie inside `in` (THD_ERR_ALIAS).  0 bytes is THD_OK with
+ * no launch.  Stream-ordered, one launch each.
+ */
+int thd_read_stream(const void* in, int64_t bytes, const void* key, uint32_t* count, void* stream);
+int thd_write_stream(void* out, int64_t bytes, uint32_t seed, void* stream);
+
 /* thd_strerror -- static text for a return or status code. */
 const char* thd_strerror(int32_t code);
 

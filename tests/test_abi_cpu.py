@@ -106,6 +106,20 @@ def test_host_rejections_without_device_work(pkg):
     assert lib.thd_copy(None, 1 << 24, 16, None) == pkg.THD_ERR_ARG
     assert lib.thd_copy(1 << 20, (1 << 20) + 8, 16, None) == pkg.THD_ERR_ALIAS
     assert lib.thd_copy(None, None, 0, None) == pkg.THD_OK
+    # read and write streams: size a multiple of 16, aligned pointers, no overlap
+    key = ctypes.create_string_buffer(16)
+    assert lib.thd_read_stream(1 << 20, 24, key, 1 << 24, None) == pkg.THD_ERR_ARG
+    assert lib.thd_read_stream(1 << 20, -16, key, 1 << 24, None) == pkg.THD_ERR_ARG
+    assert lib.thd_read_stream((1 << 20) + 8, 16, key, 1 << 24, None) == pkg.THD_ERR_ARG
+    assert lib.thd_read_stream(1 << 20, 16, key, None, None) == pkg.THD_ERR_ARG
+    assert lib.thd_read_stream(1 << 20, 16, None, 1 << 24, None) == pkg.THD_ERR_ARG
+    assert lib.thd_read_stream(1 << 20, 16, key, (1 << 24) + 2, None) == pkg.THD_ERR_ARG
+    assert lib.thd_read_stream(1 << 20, 32768, key, (1 << 20) + 32764, None) == pkg.THD_ERR_ALIAS
+    assert lib.thd_read_stream(None, 0, None, None, None) == pkg.THD_OK
+    assert lib.thd_write_stream(1 << 20, 24, 0, None) == pkg.THD_ERR_ARG
+    assert lib.thd_write_stream((1 << 20) + 4, 16, 0, None) == pkg.THD_ERR_ARG
+    assert lib.thd_write_stream(None, 16, 0, None) == pkg.THD_ERR_ARG
+    assert lib.thd_write_stream(None, 0, 0, None) == pkg.THD_OK
     # tuning argument checks
     assert lib.thd_swap_tuning(-1, 0, 1, 0, 0) == pkg.THD_ERR_ARG
     assert lib.thd_swap_tuning(0, -1, 1, 0, 0) == pkg.THD_ERR_ARG

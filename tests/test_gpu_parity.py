@@ -273,6 +273,42 @@ def test_plain_copy(thd, nbytes, offset):
     assert (dst[:offset] == 7).all() and (dst[offset + nbytes:] == 7).all()
 
 
+@pytest.mark.parametrize("nwords", [1, 127, 128, 129, 255, 256, 257, 256 * 37 + 5, 1 << 18])
+def test_read_and_write_streams(thd, nwords):
+    # The two streaming ceilings.  Read: the key is planted at the first and
+    # last word, at tile borders and at random places of a random buffer, and
+    # the count must equal NumPy's count of equal 16-byte words (added to what
+    # the counter held).  Write: word w = four copies of w ^ seed, guard words
+    # around the destination untouched.  Ragged last tiles throughout.
+    import torch
+    nbytes = 16 * nwords
+    g = torch.Generator(device="cuda").manual_seed(nwords)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    key = bytes(range(7, 23))
+    rng = np.random.default_rng(nwords)
+    spots = {0, nwords - 1, min(nwords - 1, 255), min(nwords - 1, 256), min(nwords - 1, 127)}
+    spots |= set(rng.integers(0, nwords, size=min(nwords, 9)).tolist())
+    kt = torch.tensor(list(key), dtype=torch.uint8, device="cuda")
+    for w in spots:
+        src[16 * w:16 * w + 16] = kt
+    count = torch.tensor([5], dtype=torch.int32, device="cuda")
+    say("read stream", nwords)
+    assert thd.thd_read_stream(src, nbytes, key, count) == thd.THD_OK
+    words = src.cpu().numpy().reshape(-1, 16)
+    expect = int((words == np.frombuffer(key, np.uint8)).all(axis=1).sum())
+    assert expect >= len(spots)
+    assert int(count.item()) == 5 + expect
+
+    seed = 0x9E3779B9
+    dst = torch.full((nbytes + 64,), 7, dtype=torch.uint8, device="cuda")
+    say("write stream", nwords)
+    assert thd.thd_write_stream(dst[32:32 + nbytes], nbytes, seed) == thd.THD_OK
+    got = dst.cpu().numpy()
+    w = (np.arange(nwords, dtype=np.uint64) & 0xFFFFFFFF).astype(np.uint32) ^ np.uint32(seed)
+    assert np.array_equal(got[32:32 + nbytes].view(np.uint32).reshape(-1, 4), np.repeat(w[:, None], 4, axis=1))
+    assert (got[:32] == 7).all() and (got[32 + nbytes:] == 7).all()
+
+
 @pytest.mark.parametrize("seed,cp,docs,max_chunk,n_empty,rb", [
     (400, 4, 290, 2, 10, 8),      # ~2400 segments: the one-launch build writes the directory
     (401, 16, 60, 3, 4, 4096),    # cp 16, many directory workgroups, 4 KiB rows
