@@ -171,6 +171,41 @@ def test_maximum_size_swap(thd):
     torch.cuda.empty_cache()
 
 
+def test_maximum_size_swap_wide_rows(thd):
+    # T = 2**31 - 64 tokens of 16-byte rows (the widest copy unit): 32 GiB
+    # per buffer, so every byte offset past 2**31 and 2**32 is exercised on
+    # the 4 KiB-tile path.  Sampled rows against the oracle's single-token
+    # form, every run's first and last token included; then the round trip.
+    import torch
+    cp = 4
+    total = 2 ** 31 - 64
+    lens = [1 << 30, 8, 0, 536870912, 24, total - (1 << 30) - 536870912 - 32]
+    assert all(v % (2 * cp) == 0 for v in lens) and sum(lens) == total
+    cu = W.cumulative(lens)
+    say("maximum size, 16-byte rows", total)
+    route = thd.Route(len(lens), cp, total)
+    route.build(dev_i32(cu), cp, total)
+    assert route.status() == 0
+    by_src, _, _ = route.copy_out()
+    g = torch.Generator(device="cuda").manual_seed(W.BASE_SEED + 41)
+    x = torch.empty((total, 16), dtype=torch.uint8, device="cuda")
+    x.view(torch.int64).random_(generator=g)
+    out = route.swap(x, thd.Z2C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([rng.integers(0, total, 3000), by_src[:, 1].astype(np.int64),
+                                     by_src[:, 1].astype(np.int64) + by_src[:, 2] - 1, [0, total - 1]]))
+    src = np.array([O.zigzag_position(cu, cp, total, int(t)) for t in toks], dtype=np.int64)
+    got = out.index_select(0, torch.from_numpy(toks).cuda()).cpu().numpy()
+    want = x.index_select(0, torch.from_numpy(src).cuda()).cpu().numpy()
+    assert np.array_equal(got, want)
+    back = route.swap(out, thd.C2Z)
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    del x, out, back, route
+    torch.cuda.empty_cache()
+
+
 def test_maximum_size_roll(thd):
     # T = 2**31 - 64 positions, two shifts: the label and MTP outputs reach
     # 2 x 16 GiB, so every index past 2**31 is exercised.  Checked at sampled
