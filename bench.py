@@ -349,9 +349,9 @@ def main():
     swap_gbps = swap_bytes / (swap_avg_ms * 1e-3) / 1e9
 
     # route build and roll device times: events around single launches, after the timed region
-    build_ms = _event_samples(torch, stream, lambda: thd.thd_build_route(h, cu, n_slots, cp, total, s_handle), 50)
+    build_ms = _event_samples(torch, stream, lambda: thd.thd_build_route(h, cu, n_slots, cp, total, s_handle), 100)
     roll_ms = _event_samples(torch, stream, lambda: thd.thd_roll_labels(ids, cu, cu_real, n_slots, total, j, 0,
-                                                                        shifted, mask, status, s_handle), 50)
+                                                                        shifted, mask, status, s_handle), 100)
 
     # route build: host enqueue time of the build call alone (device time from the events above)
     torch.cuda.synchronize()
@@ -395,8 +395,10 @@ def main():
     by_dir = {}
     for d, fn in (("z2c", lambda: thd.thd_swap(h, thd.Z2C, x, a, total, rb, s_handle)),
                   ("c2z", lambda: thd.thd_swap(h, thd.C2Z, a, b, total, rb, s_handle))):
-        fn()
-        by_dir[d] = round(_median_event_ms(torch, stream, fn, 20) * 1e3, 2)
+        for _ in range(3):
+            fn()
+        ts = _event_samples(torch, stream, fn, 20)
+        by_dir[d] = {"median": round(float(np.median(ts)) * 1e3, 2), "min": round(float(np.min(ts)) * 1e3, 2)}
     stream_copy_gbps = swap_bytes / (copy_stream_ms * 1e-3) / 1e9
 
     def step_on(s):
