@@ -5,6 +5,47 @@
 
 namespace thdcp {
 
+// Inclusive scan of one 64-lane wave with DPP lane moves instead of LDS
+// permutes: four row_shr steps (1, 2, 4, 8) scan each row of 16 lanes, then
+// row_bcast:15 carries each row's last lane into the next row (rows 1 and 3)
+// and row_bcast:31 carries lane 31 into rows 2 and 3.  A lane whose source
+// is outside its row, or whose row the step does not write, takes
+// `identity`.  op must be associative with `identity` as its neutral value.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int32_t dpp_move(int32_t x, int32_t old) {
+  return __builtin_amdgcn_update_dpp(old, x, kCtrl, kRowMask, 0xf, false);
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int64_t dpp_move(int64_t x, int64_t old) {
+  const int32_t lo = __builtin_amdgcn_update_dpp(static_cast<int32_t>(old), static_cast<int32_t>(x), kCtrl,
+                                                 kRowMask, 0xf, false);
+  const int32_t hi = __builtin_amdgcn_update_dpp(static_cast<int32_t>(old >> 32), static_cast<int32_t>(x >> 32),
+                                                 kCtrl, kRowMask, 0xf, false);
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                              static_cast<uint32_t>(lo));
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_inclusive_scan(T x, T identity, Op op) {
+  x = op(x, dpp_move<0x111, 0xf>(x, identity));  // row_shr:1
+  x = op(x, dpp_move<0x112, 0xf>(x, identity));  // row_shr:2
+  x = op(x, dpp_move<0x114, 0xf>(x, identity));  // row_shr:4
+  x = op(x, dpp_move<0x118, 0xf>(x, identity));  // row_shr:8
+  x = op(x, dpp_move<0x142, 0xa>(x, identity));  // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_move<0x143, 0xc>(x, identity));  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+struct ScanAdd {
+  template <typename T>
+  __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+struct ScanMax {
+  template <typename T>
+  __device__ __forceinline__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+
 // Exclusive prefix sum over a workgroup of kThreads threads (a multiple of
 // 64, at most 1024).  Every thread must call it.  Returns the thread's
 // exclusive offset and stores the workgroup total in *total.  s_wave is LDS
@@ -14,22 +55,12 @@ __device__ T block_exclusive_scan(T v, T* s_wave, T* total) {
   constexpr int kWaves = kThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  T x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const T x = wave_inclusive_scan(v, T(0), ScanAdd{});
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   if (wave == 0) {
     const T w = lane < kWaves ? s_wave[lane] : T(0);
-    T xs = w;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const T y = __shfl_up(xs, o, 64);
-      if (lane >= o) xs += y;
-    }
+    const T xs = wave_inclusive_scan(w, T(0), ScanAdd{});
     if (lane < kWaves) s_wave[lane] = xs - w;
     if (lane == kWaves - 1) s_wave[kWaves] = xs;
   }
@@ -52,14 +83,9 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
   const int wave = threadIdx.x >> 6;
   int64_t x[K], ex[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) x[k] = v[k];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t y = __shfl_up(x[k], o, 64);
-      if (lane >= o) x[k] = kMax ? (x[k] > y ? x[k] : y) : x[k] + y;
-    }
+  for (int k = 0; k < K; ++k) {
+    if constexpr (kMax) x[k] = wave_inclusive_scan(v[k], identity, ScanMax{});
+    else x[k] = wave_inclusive_scan(v[k], identity, ScanAdd{});
   }
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -72,12 +98,9 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t w = lane < kWaves ? s[k * (kWaves + 1) + lane] : identity;
-      int64_t xs = w;
-#pragma unroll
-      for (int o = 1; o < kWaves; o <<= 1) {
-        const int64_t y = __shfl_up(xs, o, 64);
-        if (lane >= o) xs = kMax ? (xs > y ? xs : y) : xs + y;
-      }
+      int64_t xs;
+      if constexpr (kMax) xs = wave_inclusive_scan(w, identity, ScanMax{});
+      else xs = wave_inclusive_scan(w, identity, ScanAdd{});
       int64_t prev = __shfl_up(xs, 1, 64);
       if (lane == 0) prev = identity;
       if (lane < kWaves) s[k * (kWaves + 1) + lane] = prev;
