@@ -89,8 +89,7 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
   }
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    ex[k] = __shfl_up(x[k], 1, 64);
-    if (lane == 0) ex[k] = identity;
+    ex[k] = dpp_move<0x138, 0xf>(x[k], identity);  // wave_shr:1, lane 0 takes identity
     if (lane == 63) s[k * (kWaves + 1) + wave] = x[k];
   }
   __syncthreads();
@@ -101,8 +100,7 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
       int64_t xs;
       if constexpr (kMax) xs = wave_inclusive_scan(w, identity, ScanMax{});
       else xs = wave_inclusive_scan(w, identity, ScanAdd{});
-      int64_t prev = __shfl_up(xs, 1, 64);
-      if (lane == 0) prev = identity;
+      const int64_t prev = dpp_move<0x138, 0xf>(xs, identity);
       if (lane < kWaves) s[k * (kWaves + 1) + lane] = prev;
       if (lane == kWaves - 1) s[k * (kWaves + 1) + kWaves] = xs;
     }
