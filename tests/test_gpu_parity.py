@@ -224,6 +224,7 @@ def test_worked_example_on_gpu(thd, golden):
     (203, 3, 2500, 1, 40),
     (204, 2, 14000, 2, 300),      # 3 * n_slots words above the LDS budget: global scratch
     (205, 256, 4, 2, 1),          # cp^2 above the LDS budget: global scratch
+    (206, 1024, 3, 2, 1),         # cp at THD_MAX_CP: a 4 MiB split matrix in global scratch
 ])
 def test_route_build_slow_paths(thd, seed, cp, docs, max_chunk, n_empty):
     import torch
