@@ -1,0 +1,140 @@
+"""Seeded random sweeps on the GPU against the CPU oracle, byte for byte.
+
+Many small batches drawn from one seeded generator, each through one device
+call and compared whole with the oracle: cp from 1 to 64, 1-80 documents with
+chunks of 1-64 tokens, empty slots anywhere, rows of 1-4112 bytes at byte
+offsets that force every copy unit (16/8/4/2/1 B), both directions; several
+tensors through one launch; label rolls with real lengths shorter than the
+padded ones, in natural and in zigzag order.  Each case is printed before it
+runs, and every assertion names its case.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import dev_i32, dev_i64, say
+
+pytestmark = pytest.mark.gpu
+
+ROW_BYTES = [1, 2, 3, 4, 6, 8, 12, 16, 20, 32, 48, 64, 100, 256, 1000, 4096, 4112]
+CPS = [1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64]
+OFFSETS = [0, 0, 0, 1, 2, 4, 8]
+
+
+@pytest.fixture(scope="module")
+def thd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import context_packed_sequence_amd as thd
+    return thd
+
+
+def draw_batch(rng, cp, max_tokens):
+    docs = int(rng.integers(1, 81))
+    max_chunk = int(rng.integers(1, 65))
+    while docs > 1 and 2 * cp * max_chunk * docs > 2 * max_tokens:
+        docs = max(1, docs // 2)
+        max_chunk = max(1, max_chunk // 2)
+    return docs, max_chunk, int(rng.integers(0, 11))
+
+
+def test_fuzz_swap(thd):
+    import torch
+    rng = np.random.default_rng([W.BASE_SEED, 900])
+    for case in range(160):
+        cp = int(rng.choice(CPS))
+        rb = int(rng.choice(ROW_BYTES))
+        offset = int(rng.choice(OFFSETS))
+        docs, max_chunk, n_empty = draw_batch(rng, cp, 200000 // max(rb, 16))
+        w = W.random_packed([901, case], cp, docs, max_chunk, n_empty, row_shape=(rb,), row_dtype="uint8")
+        total = w.total
+        tag = f"swap case {case}: cp {cp} docs {docs} chunk<={max_chunk} empty {n_empty} rb {rb} off {offset} T {total}"
+        say(tag)
+        route = thd.Route(max(1, w.n_slots), cp, max(total, 1))
+        route.build(dev_i32(w.cu_padded), cp, total)
+        assert route.status() == 0, tag
+        x_host = w.rows_host()
+        nbytes = total * rb
+        in_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+        out_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+        in_buf[offset:offset + nbytes] = torch.from_numpy(x_host.reshape(-1)).cuda()
+        for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+            out_buf.fill_(0xA5)
+            code = thd.thd_swap(route.handle, d, in_buf.data_ptr() + offset, out_buf.data_ptr() + offset, total, rb)
+            torch.cuda.synchronize()
+            got = out_buf.cpu().numpy()
+            if cp == 1:
+                assert code == thd.THD_IDENTITY, tag
+                assert (got == 0xA5).all(), tag  # nothing written
+                continue
+            assert code == thd.THD_OK, tag
+            want = O.swap_rows(x_host, w.cu_padded, cp, total, direction).reshape(-1)
+            assert np.array_equal(got[offset:offset + nbytes], want), f"{tag} {direction}"
+            assert (got[:offset] == 0xA5).all() and (got[offset + nbytes:] == 0xA5).all(), f"{tag} {direction}"
+        route.close()
+
+
+def test_fuzz_swap_batch(thd):
+    import torch
+    rng = np.random.default_rng([W.BASE_SEED, 910])
+    for case in range(50):
+        cp = int(rng.choice(CPS[1:]))
+        docs, max_chunk, n_empty = draw_batch(rng, cp, 8000)
+        w = W.random_packed([911, case], cp, docs, max_chunk, n_empty, row_shape=(1,), row_dtype="uint8")
+        total = w.total
+        n = int(rng.integers(1, 7))
+        rbs = [int(rng.choice(ROW_BYTES[:-2])) for _ in range(n)]
+        direction = ["z2c", "c2z"][int(rng.integers(0, 2))]
+        tag = f"batch case {case}: cp {cp} T {total} row bytes {rbs} {direction}"
+        say(tag)
+        route = thd.Route(max(1, w.n_slots), cp, max(total, 1))
+        route.build(dev_i32(w.cu_padded), cp, total)
+        hosts = [np.random.default_rng([912, case, i]).integers(0, 256, (total, rb), dtype=np.uint8)
+                 for i, rb in enumerate(rbs)]
+        ins = [torch.from_numpy(h).cuda() for h in hosts]
+        outs = [torch.full_like(t, 0x5A) for t in ins]
+        code = thd.thd_swap_batch(route.handle, thd.Z2C if direction == "z2c" else thd.C2Z, ins, outs, rbs, total)
+        assert code == thd.THD_OK, tag
+        torch.cuda.synchronize()
+        for i, (h, o) in enumerate(zip(hosts, outs)):
+            assert np.array_equal(o.cpu().numpy(), O.swap_rows(h, w.cu_padded, cp, total, direction)), f"{tag} #{i}"
+        route.close()
+
+
+def test_fuzz_roll(thd):
+    import torch
+    rng = np.random.default_rng([W.BASE_SEED, 920])
+    for case in range(60):
+        cp = int(rng.choice(CPS[1:9]))
+        docs, max_chunk, n_empty = draw_batch(rng, cp, 20000)
+        pad_max = int(rng.integers(0, 2 * cp * max_chunk + 1))
+        j = int(rng.integers(1, 9))
+        fill = int(rng.integers(-3, 4))
+        w = W.random_packed([921, case], cp, docs, max_chunk, n_empty, pad_max=pad_max)
+        total = w.total
+        tag = f"roll case {case}: cp {cp} T {total} slots {w.n_slots} pad<={pad_max} shifts {j} fill {fill}"
+        say(tag)
+        ids = w.ids()
+        want_s, want_m = O.roll_labels(ids, w.cu_padded, w.cu_real, total, j, fill)
+        shifted, mask, status = thd.roll_labels(dev_i64(ids), dev_i32(w.cu_padded), dev_i32(w.cu_real), j, fill)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, tag
+        assert np.array_equal(shifted.cpu().numpy(), want_s), tag
+        assert np.array_equal(mask.cpu().numpy(), want_m), tag
+        # the same roll written in zigzag order: the natural-order result sliced
+        # to zigzag rows by the oracle's c->z swap
+        route = thd.Route(max(1, w.n_slots), cp, max(total, 1))
+        route.build(dev_i32(w.cu_padded), cp, total)
+        shifted, mask, status = route.roll_labels_zigzag(dev_i64(ids), dev_i32(w.cu_padded), dev_i32(w.cu_real), j,
+                                                         fill)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, tag
+        for k in range(j):
+            assert np.array_equal(shifted[k].cpu().numpy(),
+                                  O.swap_rows(want_s[k], w.cu_padded, cp, total, "c2z")), f"{tag} shift {k + 1}"
+        for k in range(j + 1):
+            assert np.array_equal(mask[k].cpu().numpy(),
+                                  O.swap_rows(want_m[k], w.cu_padded, cp, total, "c2z")), f"{tag} mask {k}"
+        route.close()
