@@ -50,6 +50,14 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+// Typical run length of the last build, in rows: its tokens over its 2 * cp
+// zigzag segments per slot (empty slots counted, so never an overestimate of
+// the average segment).  Chooses the swap path for one-unit rows.
+int64_t typical_run_rows(const thd_route* r) {
+  const int64_t segments = 2LL * r->cp * (r->n_slots > 0 ? r->n_slots : 1);
+  return r->total / segments;
+}
+
 int check_roll_args(const int64_t* ids, const int32_t* cu_pad, int32_t n_slots, int64_t total, int32_t max_shift,
                     const int64_t* shifted, const uint8_t* mask, const int32_t* status) {
   if (!cu_pad || n_slots < 0 || total < 0 || total > INT32_MAX) return THD_ERR_ARG;
@@ -189,8 +197,8 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
   const RunPair* runs = z2c ? route->dev.runs_dst : route->dev.runs_src;
   const thdcp::DirEntry* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
   const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
-  if (thdcp::launch_swap(route->dev.hdr, runs, word, dir, in, out, static_cast<int32_t>(rows), row_bytes, g_swap_cfg,
-                         as_stream(stream)) != hipSuccess)
+  if (thdcp::launch_swap(route->dev.hdr, runs, word, dir, in, out, static_cast<int32_t>(rows), row_bytes,
+                         typical_run_rows(route), g_swap_cfg, as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;
   return THD_OK;
 }
@@ -279,7 +287,7 @@ int thd_swap_batch(const thd_route* route, int32_t direction, int32_t n_tensors,
   const thdcp::DirEntry* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
   const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
   if (thdcp::launch_swap_batch(route->dev.hdr, runs, word, dir, n_tensors, ins, outs, row_bytes,
-                               static_cast<int32_t>(rows), as_stream(stream)) != hipSuccess)
+                               static_cast<int32_t>(rows), typical_run_rows(route), as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;
   return THD_OK;
 }

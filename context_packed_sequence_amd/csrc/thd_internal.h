@@ -84,13 +84,18 @@ hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunc
 hipError_t launch_read_stream(const void* in, int64_t bytes, const uint32_t key[4], uint32_t* count,
                               hipStream_t stream);
 hipError_t launch_write_stream(void* out, int64_t bytes, uint32_t seed, hipStream_t stream);
+// run_rows: the typical run length in rows the host expects (total rows over
+// the 2 * cp * n_slots zigzag segments).  Rows of exactly one copy unit go
+// through the LDS-staged small-row path when runs are shorter than one tile
+// of the piecewise path, and through the piecewise path (a tile is then one
+// or two flat copies) when they are at least that long.
 hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
-                       const void* in, void* out, int32_t total, int64_t row_bytes,
+                       const void* in, void* out, int32_t total, int64_t row_bytes, int64_t run_rows,
                        const SwapLaunch& cfg, hipStream_t stream);
 
 hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                              int32_t n, const void* const* ins, void* const* outs, const int64_t* row_bytes,
-                             int32_t total, hipStream_t stream);
+                             int32_t total, int64_t run_rows, hipStream_t stream);
 
 // Token-order runs of a route, for writing the roll's outputs in zigzag order.
 struct RollRoute {

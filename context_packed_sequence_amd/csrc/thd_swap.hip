@@ -242,6 +242,7 @@ struct BatchTensor {
   int32_t unit;        // copy unit in bytes: 16, 8, 4, 2 or 1
   int32_t parts;       // > 1: each tile is one part of one row, part_bytes long
   int64_t part_bytes;
+  int32_t small;       // one-unit rows of 1-8 B with short runs: the LDS-staged path
 };
 
 struct BatchArgs {
@@ -278,9 +279,8 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
     }
     const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(g - bt.first_tile) * bt.tile_rows);
     const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + bt.tile_rows));
-    if (bt.row_bytes == bt.unit) {  // one unit per row: the LDS-staged small-row path
+    if (bt.small) {  // one unit per row, short runs: the LDS-staged small-row path
       switch (bt.unit) {
-        case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, 16, r0, r1); break;
         case 8: swap_tile_small<u32x2, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
         case 4: swap_tile_small<uint32_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
         case 2: swap_tile_small<uint16_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
@@ -348,11 +348,17 @@ hipError_t launch_typed(const int32_t* hdr, const RunPair* runs, int runs_word, 
 }  // namespace
 
 hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir, const void* in,
-                       void* out, int32_t total, int64_t row_bytes, const SwapLaunch& cfg, hipStream_t stream) {
+                       void* out, int32_t total, int64_t row_bytes, int64_t run_rows, const SwapLaunch& cfg,
+                       hipStream_t stream) {
   // Widest unit that divides the row size and both base addresses.
   const int unit = copy_unit(row_bytes, in, out);
 
-  if (row_bytes == unit && cfg.tile_bytes == 0 && cfg.block_threads == 0) {
+  // One-unit rows: the LDS-staged path when runs are shorter than a tile of
+  // the piecewise path (4 KiB of 16-byte rows, 8 KiB of smaller ones); with
+  // longer runs the piecewise path streams them as flat copies, 5-300 %
+  // faster on batches of 256 MiB and more.
+  const int64_t flat_tile_rows = (unit == 16 ? 4096 : 8192) / unit;
+  if (row_bytes == unit && cfg.tile_bytes == 0 && cfg.block_threads == 0 && run_rows < flat_tile_rows) {
     constexpr int kBlock = 256;
     const int64_t tiles = (static_cast<int64_t>(total) + kBlock * kSmallRowsPerThread - 1) /
                           (kBlock * kSmallRowsPerThread);
@@ -436,15 +442,17 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
 
 hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_word, const DirEntry* dir,
                              int32_t n, const void* const* ins, void* const* outs, const int64_t* row_bytes,
-                             int32_t total, hipStream_t stream) {
+                             int32_t total, int64_t run_rows, hipStream_t stream) {
   BatchArgs args{};
   args.n = n;
   int64_t tiles = 0;
   for (int32_t i = 0; i < n; ++i) {
     const int unit = copy_unit(row_bytes[i], ins[i], outs[i]);
     const int64_t tile_bytes = unit == 16 ? 4096 : 8192;
-    int64_t tile_rows = row_bytes[i] == unit ? kBatchBlock * kSmallRowsPerThread
-                                             : (tile_bytes + row_bytes[i] - 1) / row_bytes[i];
+    // one-unit rows of 1-8 B with runs shorter than a piecewise tile: the
+    // LDS-staged path, as for thd_swap
+    const bool small = row_bytes[i] == unit && unit < 16 && run_rows < tile_bytes / unit;
+    int64_t tile_rows = small ? kBatchBlock * kSmallRowsPerThread : (tile_bytes + row_bytes[i] - 1) / row_bytes[i];
     if (tile_rows < 1) tile_rows = 1;
     if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
     // rows longer than a tile (16-byte units): every workgroup still moves
@@ -464,6 +472,7 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
     args.t[i].unit = unit;
     args.t[i].parts = static_cast<int32_t>(parts);
     args.t[i].part_bytes = part_bytes;
+    args.t[i].small = small ? 1 : 0;
     tiles += parts > 1 ? static_cast<int64_t>(total) * parts : (total + tile_rows - 1) / tile_rows;
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
   }

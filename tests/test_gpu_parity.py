@@ -257,6 +257,35 @@ def test_small_rows_with_dense_runs(thd, seed, cp, rb):
         assert np.array_equal(out.cpu().numpy(), O.swap_rows(w.rows_host(), cu, cp, total, direction)), direction
 
 
+@pytest.mark.parametrize("rb", [1, 2, 4, 8, 16])
+def test_one_unit_rows_with_long_runs(thd, rb):
+    # Rows of exactly one copy unit whose runs are longer than a tile of the
+    # piecewise path: thd_swap and thd_swap_batch stream them as flat copies
+    # instead of the LDS-staged path.  A short-document batch through the same
+    # calls keeps the staged path.  Both against the oracle, byte for byte.
+    import torch
+    cp = 2
+    for lens in ([65536, 40000, 32768 + 4, 4, 100000], [8, 12, 4] * 300):
+        cu = W.cumulative(lens)
+        total = int(cu[-1])
+        say("one-unit rows", rb, "T", total, "slots", len(lens))
+        route = thd.Route(len(lens), cp, total)
+        route.build(dev_i32(cu), cp, total)
+        hosts = [np.random.default_rng([rb, total, i]).integers(0, 256, (total, rb), dtype=np.uint8) for i in range(3)]
+        ins = [torch.from_numpy(h).cuda() for h in hosts]
+        for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+            wants = [O.swap_rows(h, cu, cp, total, direction) for h in hosts]
+            out = route.swap(ins[0], d)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), wants[0]), (rb, total, direction)
+            outs = [torch.empty_like(t) for t in ins]
+            assert thd.thd_swap_batch(route.handle, d, ins, outs, [rb] * 3, total) == thd.THD_OK
+            torch.cuda.synchronize()
+            for k in range(3):
+                assert np.array_equal(outs[k].cpu().numpy(), wants[k]), (rb, total, direction, k)
+        route.close()
+
+
 @pytest.mark.parametrize("nbytes,offset", [(1 << 20, 0), (4096 * 37 + 16, 0), (1000, 8), (999, 4), (4098, 2),
                                            (12345, 1), (3, 0)])
 def test_plain_copy(thd, nbytes, offset):
