@@ -266,7 +266,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the cross-rank exchange is "
-              "emulated as one global permutation on a single device; see DESIGN.md for how it would shard.",
+              "emulated as one global permutation on a single device; on several GPUs each rank would build "
+              "the same route locally and exchange its rows in one all-to-all-v, which is not built here.",
               file=sys.stderr)
         sys.exit(2)
 
