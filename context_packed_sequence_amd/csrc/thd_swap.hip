@@ -353,11 +353,14 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   // Widest unit that divides the row size and both base addresses.
   const int unit = copy_unit(row_bytes, in, out);
 
+  // Tile of the piecewise path for units under 16 bytes: 8 KiB, 4 KiB for
+  // 1-byte units (sweeps of 1-100-byte rows on 1 GiB swaps).
+  const int64_t unit_tile_bytes = unit == 1 ? 4096 : 8192;
+
   // One-unit rows: the LDS-staged path when runs are shorter than a tile of
-  // the piecewise path (4 KiB of 16-byte rows, 8 KiB of smaller ones); with
-  // longer runs the piecewise path streams them as flat copies, 5-300 %
-  // faster on batches of 256 MiB and more.
-  const int64_t flat_tile_rows = (unit == 16 ? 4096 : 8192) / unit;
+  // the piecewise path; with longer runs the piecewise path streams them as
+  // flat copies, 5-300 % faster on batches of 256 MiB and more.
+  const int64_t flat_tile_rows = (unit == 16 ? 4096 : unit_tile_bytes) / unit;
   if (row_bytes == unit && cfg.tile_bytes == 0 && cfg.block_threads == 0 && run_rows < flat_tile_rows) {
     constexpr int kBlock = 256;
     const int64_t tiles = (static_cast<int64_t>(total) + kBlock * kSmallRowsPerThread - 1) /
@@ -383,18 +386,20 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   }
 
   // Launch shape.  Measured on MI355X (head-to-head sweeps on one box,
-  // repeated on a second): every workgroup moves about 4 KiB.  Rows of 4 KiB
-  // up to 8 KiB: one row per 256-thread workgroup, XCD-chunked order with
-  // chunks of 128 tiles.  Rows of 8 KiB and more: 4 KiB slices of one row per
-  // 128-thread workgroup, chunks of 64.  Shorter rows: 4 KiB tiles of whole
-  // rows, 128 threads, natural order.  Every field can be overridden for
-  // sweeps; a tile size below the row size cuts rows into slices.
+  // repeated on a second): with 16-byte units every workgroup moves about
+  // 4 KiB.  Rows of 4 KiB up to 8 KiB: one row per 256-thread workgroup,
+  // XCD-chunked order with chunks of 128 tiles.  Rows of 8 KiB and more:
+  // 4 KiB slices of one row per 128-thread workgroup, chunks of 64.  Shorter
+  // rows: 4 KiB tiles of whole rows, 128 threads, natural order.  Units under
+  // 16 bytes: 256 threads, the tiles above, chunks of 64.  Every field can be
+  // overridden for sweeps; a tile size below the row size cuts rows into
+  // slices.
   const bool big_rows = unit == 16 && row_bytes >= 8192;
   const bool mid_rows = unit == 16 && row_bytes >= 4096 && !big_rows;
   const int64_t tile_bytes =
-      cfg.tile_bytes > 0 ? cfg.tile_bytes : (mid_rows ? row_bytes : (unit == 16 ? 4096 : 8192));
+      cfg.tile_bytes > 0 ? cfg.tile_bytes : (mid_rows ? row_bytes : (unit == 16 ? 4096 : unit_tile_bytes));
   const int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (mid_rows ? 256 : 128) : 256);
-  int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order : (big_rows ? 64 : (mid_rows ? 128 : 1));
+  int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order : (big_rows ? 64 : (mid_rows ? 128 : (unit == 16 ? 1 : 64)));
 
   int64_t tile_rows = (tile_bytes + row_bytes - 1) / row_bytes;
   if (tile_rows < 1) tile_rows = 1;
