@@ -57,13 +57,88 @@ __device__ __forceinline__ void copy_span(const U* __restrict__ src, U* __restri
   for (int64_t i = base + tid; i < n; i += BLOCK) store_unit<NT>(dst + i, load_unit<NT>(src + i));
 }
 
+// 16-byte output words from a source that is not 16-byte aligned: output
+// word j (16-byte aligned) holds source bytes [s + 16 j, s + 16 j + 16) with
+// s = a + 16 * D + B, a 16-byte aligned, D whole 4-byte words and B bytes
+// (0 < 4 * D + B < 16).  The thread loads the two aligned source words that
+// cover those bytes and funnels them together, four 32-bit byte-aligns.
+// Both aligned words hold at least one byte of the source range, so no load
+// leaves the pages the range lies in.
+template <int D, int BLOCK, int UNROLL, bool NT>
+__device__ __forceinline__ void realign_words(const u32x4* __restrict__ a, u32x4* __restrict__ dst, int64_t n,
+                                              uint32_t b) {
+  const int tid = threadIdx.x;
+  for (int64_t base = 0; base < n; base += BLOCK * UNROLL) {
+    u32x4 lo[UNROLL], hi[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t j = base + u * BLOCK + tid;
+      if (j < n) {
+        lo[u] = load_unit<NT>(a + j);
+        hi[u] = load_unit<NT>(a + j + 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t j = base + u * BLOCK + tid;
+      if (j < n) {
+        const uint32_t w[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w, hi[u].x, hi[u].y, hi[u].z, hi[u].w};
+        u32x4 o;
+        o.x = __builtin_amdgcn_alignbyte(w[D + 1], w[D], b);
+        o.y = __builtin_amdgcn_alignbyte(w[D + 2], w[D + 1], b);
+        o.z = __builtin_amdgcn_alignbyte(w[D + 3], w[D + 2], b);
+        o.w = __builtin_amdgcn_alignbyte(w[D + 4], w[D + 3], b);
+        store_unit<NT>(dst + j, o);
+      }
+    }
+  }
+}
+
+// Bytes [src, src + n) to [dst, dst + n) for pointers and sizes that are
+// multiples of sizeof(U) < 16: U-sized copies up to dst's first 16-byte
+// boundary and after its last one, 16-byte stores in between whatever the
+// source's alignment (a plain 16-byte copy when both sides share it).
+template <typename U, int BLOCK, int PAIRS, bool NT>
+__device__ __forceinline__ void copy_bytes_realigned(const unsigned char* __restrict__ src,
+                                                     unsigned char* __restrict__ dst, int64_t n) {
+  const int tid = threadIdx.x;
+  const int64_t head = min(n, static_cast<int64_t>((16 - (reinterpret_cast<uintptr_t>(dst) & 15)) & 15));
+  for (int64_t i = tid; i < head / static_cast<int64_t>(sizeof(U)); i += BLOCK)
+    store_unit<NT>(reinterpret_cast<U*>(dst) + i, load_unit<NT>(reinterpret_cast<const U*>(src) + i));
+  const int64_t words = (n - head) / 16;
+  const unsigned char* s = src + head;
+  u32x4* d = reinterpret_cast<u32x4*>(dst + head);
+  const uint32_t m = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s) & 15);
+  if (m == 0) {
+    copy_span<u32x4, BLOCK, PAIRS, NT>(reinterpret_cast<const u32x4*>(s), d, words);
+  } else {
+    const u32x4* a = reinterpret_cast<const u32x4*>(s - m);
+    switch (m >> 2) {
+      case 0: realign_words<0, BLOCK, PAIRS, NT>(a, d, words, m & 3); break;
+      case 1: realign_words<1, BLOCK, PAIRS, NT>(a, d, words, m & 3); break;
+      case 2: realign_words<2, BLOCK, PAIRS, NT>(a, d, words, m & 3); break;
+      default: realign_words<3, BLOCK, PAIRS, NT>(a, d, words, m & 3); break;
+    }
+  }
+  const int64_t done = head + 16 * words;
+  for (int64_t i = tid; i < (n - done) / static_cast<int64_t>(sizeof(U)); i += BLOCK)
+    store_unit<NT>(reinterpret_cast<U*>(dst + done) + i, load_unit<NT>(reinterpret_cast<const U*>(src + done) + i));
+}
+
+// Pieces of at least this many bytes in units under 16 bytes go through the
+// realigning copy.
+constexpr int64_t kRealignMinBytes = 256;
+
 // One tile of output rows [r0, r1): find the run holding r0 from the
 // directory (one 16-byte load covers the usual case where no run starts
 // between the directory row, a multiple of 16, and r0; otherwise the entry's
 // run-start bits name the run, and one load of it follows), then copy run
 // piece by run piece.  Every access stays inside the run table and inside
 // [0, total) rows of both buffers.
-template <typename U, int BLOCK, int UNROLL, bool NT>
+// PAIRS: source-word pairs in flight per thread in the realigning copy (two
+// source words per output word, so half a plain copy's unroll keeps the
+// registers in flight the same); 0 leaves narrow units to the plain copy.
+template <typename U, int BLOCK, int UNROLL, bool NT, int PAIRS = (UNROLL > 2 ? UNROLL / 2 : 1)>
 __device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
                                           int32_t n_runs, const unsigned char* __restrict__ in,
                                           unsigned char* __restrict__ out, int32_t total, int64_t row_bytes,
@@ -87,7 +162,16 @@ __device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, cons
     const U* src = reinterpret_cast<const U*>(in + static_cast<int64_t>(in_row) * row_bytes);
     U* dst = reinterpret_cast<U*>(out + static_cast<int64_t>(r0) * row_bytes);
     const int64_t n_units = static_cast<int64_t>(piece_end - r0) * row_bytes / static_cast<int64_t>(sizeof(U));
-    copy_span<U, BLOCK, UNROLL, NT>(src, dst, n_units);
+    if constexpr (sizeof(U) < 16 && PAIRS > 0) {
+      if (n_units * static_cast<int64_t>(sizeof(U)) >= kRealignMinBytes)
+        copy_bytes_realigned<U, BLOCK, PAIRS, NT>(reinterpret_cast<const unsigned char*>(src),
+                                                   reinterpret_cast<unsigned char*>(dst),
+                                                   n_units * static_cast<int64_t>(sizeof(U)));
+      else
+        copy_span<U, BLOCK, UNROLL, NT>(src, dst, n_units);
+    } else {
+      copy_span<U, BLOCK, UNROLL, NT>(src, dst, n_units);
+    }
     r0 = piece_end;
     if (r0 >= r1 || ++k >= n_runs) break;
     const RunPair run = runs[k];
@@ -171,7 +255,7 @@ __device__ __forceinline__ void swap_tile_small(const RunPair* __restrict__ runs
       if (r < r1) store_unit<NT>(out + r, v[m]);
     }
   } else {
-    swap_tile<U, BLOCK, 8, NT>(runs, dir, n_runs, in8, out8, total, static_cast<int64_t>(sizeof(U)), r0, r1);
+    swap_tile<U, BLOCK, 8, NT, 0>(runs, dir, n_runs, in8, out8, total, static_cast<int64_t>(sizeof(U)), r0, r1);
   }
   __syncthreads();  // the next tile reuses s_runs and s_k
 }
@@ -290,10 +374,10 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
     }
     switch (bt.unit) {
       case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 8: swap_tile<u32x2, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 4: swap_tile<uint32_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 2: swap_tile<uint16_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      default: swap_tile<uint8_t, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 8: swap_tile<u32x2, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 4: swap_tile<uint32_t, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 2: swap_tile<uint16_t, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      default: swap_tile<uint8_t, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
     }
   }
 }
