@@ -437,9 +437,9 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   // Widest unit that divides the row size and both base addresses.
   const int unit = copy_unit(row_bytes, in, out);
 
-  // Tile of the piecewise path for units under 16 bytes: 8 KiB, 4 KiB for
-  // 1-byte units (sweeps of 1-100-byte rows on 1 GiB swaps).
-  const int64_t unit_tile_bytes = unit == 1 ? 4096 : 8192;
+  // Tile of the piecewise path for units under 16 bytes: 8 KiB (sweeps of
+  // 1-100-byte rows on 1 GiB swaps, with the realigning copy).
+  const int64_t unit_tile_bytes = 8192;
 
   // One-unit rows: the LDS-staged path when runs are shorter than a tile of
   // the piecewise path; with longer runs the piecewise path streams them as
