@@ -41,7 +41,59 @@ def parse():
     p.add_argument("--workload", default="gdn128k")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--row-sweep", action="store_true",
+                   help="instead of the step benchmark: swap and plain-copy bandwidth for a range of row sizes, "
+                        "one JSON line per size")
     return p.parse_args()
+
+
+ROW_SWEEP_BYTES = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 64, 100, 128, 256, 512, 1024, 2048, 4096, 6144, 8192,
+                   16384, 65536)
+
+
+def row_sweep(workloads):
+    """Swap bandwidth against row size: the 128K workload's document mix
+    scaled so that one swap moves about 1 GiB, every row size through the
+    same route shape; a plain copy of the same bytes alongside."""
+    import numpy as np
+    import torch
+
+    import context_packed_sequence_amd as thd
+
+    base = workloads.make("gdn128k")
+    lens = np.diff(base.cu_padded).astype(np.int64)
+    cp = base.cp
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for rb in ROW_SWEEP_BYTES:
+        scale = ((1 << 29) // rb) / lens.sum()
+        new = [int(v * scale) // (2 * cp) * (2 * cp) for v in lens]
+        cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+        total = int(cu[-1])
+        route = thd.Route(len(new), cp, total).build(torch.from_numpy(cu).cuda(), cp, total, sh)
+        g = torch.Generator(device="cuda").manual_seed(workloads.BASE_SEED + rb)
+        x = torch.randint(0, 256, (total, rb), dtype=torch.uint8, device="cuda", generator=g)
+        a = torch.empty_like(x)
+        b = torch.empty_like(x)
+        nbytes = total * rb
+        swaps = [lambda: thd.thd_swap(route.handle, thd.Z2C, x, a, total, rb, sh),
+                 lambda: thd.thd_swap(route.handle, thd.C2Z, a, b, total, rb, sh)]
+        for f in swaps * 2:
+            f()
+        torch.cuda.synchronize()
+        assert torch.equal(b, x), rb
+        t_swap = _median_event_ms(torch, stream, lambda: [f() for f in swaps], 10) / 2
+        thd.thd_copy(x, a, nbytes, sh)
+        t_copy = _median_event_ms(torch, stream, lambda: thd.thd_copy(x, a, nbytes, sh), 10)
+        swap_gbps = 2 * nbytes / (t_swap * 1e-3) / 1e9
+        copy_gbps = 2 * nbytes / (t_copy * 1e-3) / 1e9
+        print(json.dumps({"row_bytes": rb, "tokens": total, "cp_size": cp, "swap_us": round(t_swap * 1e3, 2),
+                          "swap_gbps": round(swap_gbps, 1), "frac_of_peak": round(swap_gbps / HBM_PEAK_GBPS, 4),
+                          "copy_gbps": round(copy_gbps, 1), "swap_over_copy": round(swap_gbps / copy_gbps, 4)}),
+              flush=True)
+        route.close()
+        del x, a, b
+        torch.cuda.empty_cache()
 
 
 def step_bytes(w, layers):
@@ -277,6 +329,9 @@ def main():
     import context_packed_sequence_amd as thd
     import workloads
 
+    if args.row_sweep:
+        row_sweep(workloads)
+        return
     w = workloads.make(args.workload)
     layers = w.layers
     total, cp = w.total, w.cp
