@@ -490,20 +490,33 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   // repeated on a second): with 16-byte units every workgroup moves about
   // 4 KiB.  Rows of 4 KiB up to 8 KiB: one row per 256-thread workgroup,
   // XCD-chunked order with chunks of 128 tiles.  Rows of 8 KiB and more:
-  // 4 KiB slices of one row per 128-thread workgroup, chunks of 64.  Shorter
-  // rows: 4 KiB tiles of whole rows, 128 threads, natural order.  Units under
-  // 16 bytes: 256 threads, the tiles above, chunks of 64.  Every field can be
-  // overridden for sweeps; a tile size below the row size cuts rows into
-  // slices.
+  // 4 KiB slices of one row (whole 128-byte lines where the row is made of
+  // them) per 128-thread workgroup, chunks of 64.  Rows of 1-4 KiB: see
+  // below.  Shorter rows: 4 KiB tiles of whole rows, 128 threads, natural
+  // order.  Units under 16 bytes: 256 threads, 8 KiB tiles, chunks of 64.
+  // Every field can be overridden for sweeps; a tile size below the row
+  // size cuts rows into slices.
   const bool big_rows = unit == 16 && row_bytes >= 8192;
   const bool mid_rows = unit == 16 && row_bytes >= 4096 && !big_rows;
+  // rows between 1 and 4 KiB that are not powers of two: rows of whole
+  // 128-byte lines are grouped into tiles of at least 4 KiB on 256 threads,
+  // as the 4-8 KiB rows; other sizes go one row per 128-thread workgroup
+  // (1 KiB and 2 KiB rows keep the 4 KiB tiles of the shorter rows)
+  const bool kib_rows =
+      unit == 16 && row_bytes > 1024 && row_bytes < 4096 && (row_bytes & (row_bytes - 1)) != 0;
+  const bool kib_lines = kib_rows && row_bytes % 128 == 0;
   const int64_t tile_bytes =
-      cfg.tile_bytes > 0 ? cfg.tile_bytes : (mid_rows ? row_bytes : (unit == 16 ? 4096 : unit_tile_bytes));
-  const int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (mid_rows ? 256 : 128) : 256);
-  int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order : (big_rows ? 64 : (mid_rows ? 128 : (unit == 16 ? 1 : 64)));
+      cfg.tile_bytes > 0 ? cfg.tile_bytes
+                         : (mid_rows || (kib_rows && !kib_lines) ? row_bytes : (unit == 16 ? 4096 : unit_tile_bytes));
+  const int block = cfg.block_threads > 0 ? cfg.block_threads
+                                          : (unit == 16 ? (mid_rows || kib_lines ? 256 : 128) : 256);
+  int64_t chunk = cfg.tile_order > 0
+                      ? cfg.tile_order
+                      : (kib_rows ? (kib_lines ? 128 : 64) : (big_rows ? 64 : (mid_rows ? 128 : (unit == 16 ? 1 : 64))));
 
-  int64_t tile_rows = cfg.tile_bytes == 0 && !mid_rows && !big_rows ? whole_row_tile(row_bytes, tile_bytes)
-                                                                     : (tile_bytes + row_bytes - 1) / row_bytes;
+  int64_t tile_rows = cfg.tile_bytes == 0 && !mid_rows && !big_rows && !kib_rows
+                          ? whole_row_tile(row_bytes, tile_bytes)
+                          : (tile_bytes + row_bytes - 1) / row_bytes;
   if (tile_rows < 1) tile_rows = 1;
   if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
   Shape sh;
@@ -513,7 +526,9 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   int64_t n_tiles = (total + tile_rows - 1) / tile_rows;
   if (unit == 16 && tile_bytes < row_bytes) {  // tiles are slices of one row
     int64_t parts = (row_bytes + tile_bytes - 1) / tile_bytes;
-    sh.part_bytes = ((row_bytes + parts - 1) / parts + 15) / 16 * 16;
+    // slices of whole 128-byte lines when the row is made of whole lines
+    const int64_t grain = row_bytes % 128 == 0 ? 128 : 16;
+    sh.part_bytes = ((row_bytes + parts - 1) / parts + grain - 1) / grain * grain;
     parts = (row_bytes + sh.part_bytes - 1) / sh.part_bytes;
     n_tiles = static_cast<int64_t>(total) * parts;
     if (parts > INT32_MAX || n_tiles > INT32_MAX) return hipErrorInvalidValue;
@@ -569,7 +584,8 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
     int64_t parts = 1, part_bytes = row_bytes[i];
     if (unit == 16 && row_bytes[i] > tile_bytes) {
       parts = (row_bytes[i] + tile_bytes - 1) / tile_bytes;
-      part_bytes = ((row_bytes[i] + parts - 1) / parts + 15) / 16 * 16;
+      const int64_t grain = row_bytes[i] % 128 == 0 ? 128 : 16;  // whole lines where the row has them
+      part_bytes = ((row_bytes[i] + parts - 1) / parts + grain - 1) / grain * grain;
       parts = (row_bytes[i] + part_bytes - 1) / part_bytes;
       if (parts > INT32_MAX) return hipErrorInvalidValue;
     }
