@@ -18,7 +18,8 @@ from gpu_util import dev_i32, dev_i64, say
 
 pytestmark = pytest.mark.gpu
 
-ROW_BYTES = [1, 2, 3, 4, 6, 8, 12, 16, 20, 32, 48, 64, 100, 256, 1000, 4096, 4112]
+ROW_BYTES = [1, 2, 3, 4, 6, 8, 12, 16, 20, 32, 48, 64, 100, 256, 1000, 1152, 1536, 2000, 2560, 3584, 4096, 4112,
+             10240]
 CPS = [1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64]
 OFFSETS = [0, 0, 0, 1, 2, 4, 8]
 
