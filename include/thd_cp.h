@@ -143,6 +143,12 @@ int thd_build_route(thd_route* route, const int32_t* cu_seqlens_padded, int32_t 
  * (cp_size == 1 or total_tokens == 0): the caller keeps `in` (zero copy, as
  * the pages' identity route does).  If the route's device status is an error,
  * the kernel writes nothing.  One kernel launch otherwise.
+ *
+ * The work is a bandwidth-bound copy of 2 * rows * row_bytes bytes.  Row
+ * sizes that are powers of two or multiples of 128 bytes, with 16-byte
+ * aligned buffers, run at the speed of a plain copy of the same bytes; other
+ * row sizes or alignments are moved in narrower units at a few percent to
+ * about 10 % less.
  */
 int thd_swap(const thd_route* route, int32_t direction, const void* in, void* out,
              int64_t rows, int64_t row_bytes, void* stream);
