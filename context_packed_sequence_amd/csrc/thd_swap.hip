@@ -60,29 +60,45 @@ __device__ __forceinline__ void copy_span(const U* __restrict__ src, U* __restri
 // 16-byte output words from a source that is not 16-byte aligned: output
 // word j (16-byte aligned) holds source bytes [s + 16 j, s + 16 j + 16) with
 // s = a + 16 * D + B, a 16-byte aligned, D whole 4-byte words and B bytes
-// (0 < 4 * D + B < 16).  The thread loads the two aligned source words that
-// cover those bytes and funnels them together, four 32-bit byte-aligns.
-// Both aligned words hold at least one byte of the source range, so no load
-// leaves the pages the range lies in.
+// (0 < 4 * D + B < 16).  The two aligned source words that cover those bytes
+// are funnelled together, four 32-bit byte-aligns.  Both hold at least one
+// byte of the source range, so no load leaves the pages the range lies in.
+// Every lane of the workgroup must reach this call (BLOCK a multiple of 64):
+// the lane shift reads the neighbour lane's registers.
 template <int D, int BLOCK, int UNROLL, bool NT>
 __device__ __forceinline__ void realign_words(const u32x4* __restrict__ a, u32x4* __restrict__ dst, int64_t n,
                                               uint32_t b) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   for (int64_t base = 0; base < n; base += BLOCK * UNROLL) {
-    u32x4 lo[UNROLL], hi[UNROLL];
+    // lane l of a wave takes word j and needs source words j and j + 1; word
+    // j + 1 is lane l + 1's first word, handed over by a DPP lane shift, so
+    // only the wave's last lane and the range's last word load it themselves
+    u32x4 lo[UNROLL], own_hi[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t j = base + u * BLOCK + tid;
+      lo[u] = u32x4{0u, 0u, 0u, 0u};
+      own_hi[u] = u32x4{0u, 0u, 0u, 0u};
       if (j < n) {
         lo[u] = load_unit<NT>(a + j);
-        hi[u] = load_unit<NT>(a + j + 1);
+        if (lane == 63 || j + 1 >= n) own_hi[u] = load_unit<NT>(a + j + 1);
       }
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t j = base + u * BLOCK + tid;
+      // wave_shl:1: lane l reads lane l + 1; lane 63 keeps its own word
+      const uint32_t h0 = __builtin_amdgcn_update_dpp(own_hi[u].x, lo[u].x, 0x130, 0xf, 0xf, false);
+      const uint32_t h1 = __builtin_amdgcn_update_dpp(own_hi[u].y, lo[u].y, 0x130, 0xf, 0xf, false);
+      const uint32_t h2 = __builtin_amdgcn_update_dpp(own_hi[u].z, lo[u].z, 0x130, 0xf, 0xf, false);
+      const uint32_t h3 = __builtin_amdgcn_update_dpp(own_hi[u].w, lo[u].w, 0x130, 0xf, 0xf, false);
+      // the last word of the range: its neighbour lane holds no source word
+      const bool edge = lane == 63 || j + 1 >= n;
+      const uint32_t w[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w,
+                             edge ? own_hi[u].x : h0, edge ? own_hi[u].y : h1,
+                             edge ? own_hi[u].z : h2, edge ? own_hi[u].w : h3};
       if (j < n) {
-        const uint32_t w[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w, hi[u].x, hi[u].y, hi[u].z, hi[u].w};
         u32x4 o;
         o.x = __builtin_amdgcn_alignbyte(w[D + 1], w[D], b);
         o.y = __builtin_amdgcn_alignbyte(w[D + 2], w[D + 1], b);
@@ -286,8 +302,10 @@ __global__ __launch_bounds__(BLOCK) void swap_small_kernel(const int32_t* __rest
 // back, i.e. workgroup b = 8 j + x copies tile ((j / G) * 8 + x) * G + j mod G.
 constexpr int kXcds = 8;
 
+// Capped at 64 VGPRs (8 waves per SIMD); the 16-byte-unit kernels need under
+// 50, the narrow ones 63-64 with no spills.
 template <typename U, int BLOCK, int UNROLL, bool NT>
-__global__ __launch_bounds__(BLOCK) void swap_kernel(const int32_t* __restrict__ hdr, int runs_word,
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void swap_kernel(const int32_t* __restrict__ hdr, int runs_word,
                                                      const RunPair* __restrict__ runs,
                                                      const DirEntry* __restrict__ dir,
                                                      const unsigned char* __restrict__ in,
