@@ -147,8 +147,7 @@ int thd_build_route(thd_route* route, const int32_t* cu_seqlens_padded, int32_t 
  * The work is a bandwidth-bound copy of 2 * rows * row_bytes bytes.  Row
  * sizes that are powers of two or multiples of 128 bytes, with 16-byte
  * aligned buffers, run at the speed of a plain copy of the same bytes; other
- * row sizes or alignments are moved in narrower units at a few percent to
- * about 10 % less.
+ * row sizes or alignments are moved in narrower units, at 2-7 % less.
  */
 int thd_swap(const thd_route* route, int32_t direction, const void* in, void* out,
              int64_t rows, int64_t row_bytes, void* stream);
@@ -293,23 +292,31 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
  * thd_swap_tuning -- override the swap kernel's launch shape for later calls
  * in this process (a process-wide setting; not safe to change while another
  * thread calls thd_swap).  For launch-shape sweeps: the results of thd_swap
- * never depend on it.  A 0 selects the built-in choice for that field.
+ * never depend on it.  A 0 selects the built-in choice for that field.  The
+ * built-in shapes, for rows moved in 16-byte units: rows under 1 KiB, and
+ * 1 KiB and 2 KiB rows, in tiles of about 4 KiB of whole rows (a multiple of
+ * 128 bytes where one fits) on 128 threads in natural order; other 1-4 KiB
+ * rows made of whole 128-byte lines in tiles of at least 4 KiB on 256
+ * threads, chunks of 128; the remaining 1-4 KiB rows one row per 128-thread
+ * workgroup, chunks of 64; rows of 4 KiB up to 8 KiB one row per 256-thread
+ * workgroup, chunks of 128; rows of 8 KiB and more in slices of about 4 KiB
+ * (whole 128-byte lines where the row is made of them) on 128 threads,
+ * chunks of 64.  Rows moved in narrower units: 8 KiB tiles on 256 threads,
+ * chunks of 64.  Rows of one unit (1-16 B) whose typical run is shorter than
+ * one such tile (4 KiB for 16-byte rows) take an LDS-staged kernel instead.
  *   tile_bytes      output bytes per workgroup tile, rounded up to whole rows;
  *                   with 16-byte units, a value below the row size cuts each
- *                   row into slices of about that size (built-in: 4 KiB of
- *                   whole rows under 4 KiB, one row for rows of 4 KiB up to
- *                   8 KiB, 4 KiB slices for rows of 8 KiB and more)
+ *                   row into slices of about that size
  *   max_workgroups  cap on workgroups; above it workgroups loop over tiles
  *   nontemporal     1: non-temporal loads and stores (built-in), 0: plain
- *   block_threads   128, 256, 512 or 1024 for the 16-byte path (built-in:
- *                   256 for rows of 4 KiB up to 8 KiB, 128 otherwise)
+ *   block_threads   128, 256, 512 or 1024; used by the 16-byte path only
  *   tile_order      tiles per XCD chunk: 1 = natural order (tile b to
  *                   workgroup b, so neighbouring tiles go to different
  *                   XCDs); G > 1 = XCD-chunked (tiles cut into chunks of G,
  *                   XCD x streams chunks x, x+8, ...; G >= tiles / 8
- *                   gives each XCD one contiguous eighth); built-in: 128
- *                   for rows of 4 KiB up to 8 KiB, 64 above, 1 below
- * thd_swap_tuning(0, 0, 1, 0, 0) restores the built-in shape.
+ *                   gives each XCD one contiguous eighth)
+ * A non-zero tile_bytes or block_threads also sends one-unit rows down the
+ * tiled path.  thd_swap_tuning(0, 0, 1, 0, 0) restores the built-in shape.
  */
 int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
                     int32_t tile_order);
