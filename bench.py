@@ -12,8 +12,9 @@ Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes (every
 swap reads and writes each row once; the roll reads the ids and writes its
 streams and masks) divided by the step time, in GB/s.  ``roofline`` prices the
 swap kernel (the dominant kernel) against the MI355X HBM peak; its duration is
-the mean of HIP events recorded around every swap launch in the timed region,
-on the stream the kernel runs on.  ``cpu_baseline`` times the CPU oracle on
+the mean, over the steps of the timed region, of the time between two HIP
+timing events recorded on the swap's stream just before the step's first swap
+and just after its last, divided by the step's swap count.  ``cpu_baseline`` times the CPU oracle on
 the host over a bounded sample of the same workload.
 """
 
@@ -128,11 +129,75 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+
+class TimingEvent:
+    """A HIP event used only for timing, with torch.cuda.Event's record /
+    elapsed_time interface.
+
+    Created with hipEventDisableSystemFence: recording it skips the
+    system-scope release (cache write-back and invalidate) that a default
+    event performs, which on this runtime leaves the device idle for about
+    3 us between the two kernels it separates (the flag is meant for events
+    that only time work).  The HIP runtime functions are resolved through
+    the library's handle, i.e. from the runtime the library and torch share.
+    """
+
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+
+            from context_packed_sequence_amd.binding import library
+
+            hip = library()
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+
+        self._ctypes = ctypes
+        self._hip_rt = self._runtime()
+        self._ev = ctypes.c_void_p()
+        rc = self._hip_rt.hipEventCreateWithFlags(ctypes.byref(self._ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            self._ev = None
+            raise RuntimeError(f"hipEventCreateWithFlags failed (HIP error {rc})")
+
+    def record(self, stream):
+        rc = self._hip_rt.hipEventRecord(self._ev, self._ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed (HIP error {rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end`; both must have completed."""
+        ms = self._ctypes.c_float()
+        rc = self._hip_rt.hipEventElapsedTime(self._ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed (HIP error {rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "_ev", None) is not None:
+            try:
+                self._hip_rt.hipEventDestroy(self._ev)
+            except Exception:
+                pass
+
+
 def _event_samples(torch, stream, fn, reps):
-    """Device time of fn() in ms, one sample per call, from events on the launch stream."""
+    """Device time of fn() in ms, one sample per call, from timing events on the launch stream."""
     evs = []
     for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         fn()
         b.record(stream)
@@ -356,14 +421,15 @@ def main():
     n_slots = w.n_slots
     s_handle = stream.cuda_stream
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = TimingEvent
 
     def step(e=None):
         # e: two timing events, recorded just before the first swap and just
         # after the last.  The swaps of all layers run back to back with no
-        # event between them: an event between two kernels on this runtime
-        # leaves the device idle for a few microseconds and would slow the
-        # step it measures.
+        # event between them: an event between two kernels leaves the device
+        # idle for a few microseconds (about 3 us for a timing-only event on
+        # this runtime, 6 us for a default one) and would slow the step it
+        # measures.
         thd.thd_build_route(h, cu, n_slots, cp, total, s_handle)
         if e is not None:
             e[0].record(stream)
@@ -420,7 +486,7 @@ def main():
 
     # no call waits for the GPU: hold the stream with a spin kernel, enqueue a step
     torch.cuda.synchronize()
-    gate = ev()
+    gate = torch.cuda.Event()
     torch.cuda._sleep(int(5e8))
     gate.record(stream)
     step()
