@@ -248,7 +248,7 @@ int thd_roll_labels_zigzag(const thd_route* route, const int64_t* ids, const int
                            int64_t fill, int64_t* shifted, uint8_t* mask, int32_t* status, void* stream) {
   if (!route) return THD_ERR_ARG;
   if (!route->built) return THD_ERR_NOT_BUILT;
-  if (total_tokens != route->total) return THD_ERR_SHAPE;
+  if (total_tokens != route->total || n_slots != route->n_slots) return THD_ERR_SHAPE;
   if (route->cp == 1 || total_tokens == 0)
     return thd_roll_labels(ids, cu_seqlens_padded, cu_seqlens, n_slots, total_tokens, max_shift, fill, shifted, mask,
                            status, stream);
@@ -395,6 +395,7 @@ int thd_route_copy_out(const thd_route* route, void* stream, int32_t* host_n_run
   if (hipMemcpyAsync(hdr, route->dev.hdr, sizeof(hdr), hipMemcpyDeviceToHost, s) != hipSuccess) return THD_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return THD_ERR_HIP;
   const int32_t n = hdr[thdcp::kHdrStatus] == THD_OK ? hdr[thdcp::kHdrRunsSrc] : 0;
+  if (n < 0 || n > route->run_cap) return THD_ERR_INTEGRITY;  // never after a good build
   *host_n_runs = n;
   if (n > capacity) return THD_ERR_CAPACITY;
   const int32_t cp = route->cp;

@@ -206,8 +206,8 @@ int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const 
  * §2.2 rolls labels at pack time and §2.4 slices them with the tokens).
  *
  * The route must have been built from the same cu_seqlens_padded and
- * total_tokens (THD_ERR_SHAPE if total_tokens differs, THD_ERR_NOT_BUILT if
- * never built).  Identity route (cp_size 1): same as thd_roll_labels.  If the
+ * total_tokens (THD_ERR_SHAPE if total_tokens or n_slots differs from the
+ * last build's, THD_ERR_NOT_BUILT if never built).  Identity route (cp_size 1): same as thd_roll_labels.  If the
  * route's status is an error, that code is written to `status` and nothing
  * else is written.  Other arguments, errors and outputs as thd_roll_labels.
  */
@@ -275,8 +275,10 @@ int thd_route_status(const thd_route* route, void* stream, int32_t* host_status)
  * (zigzag row, contiguous row, length) triples in emulated global rows, sorted
  * by zigzag row and by contiguous row respectively, and host_split (host
  * int32 [cp][cp]) the split matrix: split[s][d] rows go from zigzag rank s to
- * contiguous rank d.  An identity route reports 0 runs.  THD_ERR_CAPACITY if
- * `capacity` is too small (only *host_n_runs is written then).
+ * contiguous rank d.  An identity route, or one whose status is an error,
+ * reports 0 runs.  THD_ERR_CAPACITY if `capacity` is too small (only
+ * *host_n_runs is written then); THD_ERR_INTEGRITY if the device reports more
+ * runs than the route can hold (nothing is written).
  */
 int thd_route_copy_out(const thd_route* route, void* stream, int32_t* host_n_runs, int32_t capacity,
                        int32_t* host_runs_by_src, int32_t* host_runs_by_dst, int32_t* host_split);

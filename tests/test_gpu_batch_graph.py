@@ -167,6 +167,11 @@ def test_roll_zigzag_bad_route_writes_nothing(thd):
         thd.thd_roll_labels_zigzag(route.handle, torch.arange(8, device="cuda"), dev_i32([0, 8]), None, 1, 8, 1, 0,
                                    shifted, mask, status)
     assert e.value.code == thd.THD_ERR_SHAPE
+    # the same token count with another slot count is another batch too
+    with pytest.raises(thd.ThdError) as e:
+        thd.thd_roll_labels_zigzag(route.handle, torch.arange(16, device="cuda"), dev_i32([0, 16]), None, 1, 16, 1, 0,
+                                   shifted, mask, status)
+    assert e.value.code == thd.THD_ERR_SHAPE
 
 
 def test_graph_capture_replays_build_swaps_and_roll(thd):
