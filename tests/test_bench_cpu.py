@@ -25,3 +25,14 @@ def test_step_bytes_counts_every_swap_and_the_roll():
     j = w.max_shift
     assert roll == w.total * (8 + 8 * j + (j + 1))     # ids in; J shifted streams and J + 1 masks out
     assert total == 2 * w.layers * swap + roll
+
+
+def test_timing_events_resolve_the_hip_runtime_through_the_library():
+    # the bench's timing-only events call the HIP runtime the library is
+    # linked against; resolving the four entry points needs no GPU
+    sys.path.insert(0, ROOT)
+    import bench
+    hip = bench.TimingEvent._runtime()
+    for name in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime", "hipEventDestroy"):
+        assert getattr(hip, name) is not None
+    assert bench.HIP_EVENT_DISABLE_SYSTEM_FENCE == 0x20000000
