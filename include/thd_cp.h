@@ -247,7 +247,8 @@ int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq);
  *            empty (a repeated boundary).
  * workspace: device buffer of at least thd_pack_workspace_bytes(batch, seq).
  * status:    device int32 or NULL: THD_OK, THD_ERR_PACK_DOCS or
- *            THD_ERR_PACK_CAPACITY; on an error nothing but status is written.
+ *            THD_ERR_PACK_CAPACITY (THD_ERR_PACK_DOCS when both apply); on
+ *            an error nothing but status is written.
  *
  * Host errors: THD_ERR_ARG (negative sizes, seq > THD_PACK_MAX_SEQ, align < 1,
  * capacity not a multiple of align, pad_id == eod_id, null pointers,

@@ -6,7 +6,9 @@ chunks of 1-64 tokens, empty slots anywhere, rows of 1-10240 bytes at byte
 offsets that force every copy unit (16/8/4/2/1 B), both directions; the same
 under random launch-shape overrides (tile size, workgroup cap, cache policy,
 block size, tile order); several tensors through one launch; label rolls with
-real lengths shorter than the padded ones, in natural and in zigzag order.  Each case is printed before it
+real lengths shorter than the padded ones, in natural and in zigzag order;
+packs of token rows with budgets that fit, that hold too few documents, too
+few tokens, or both.  Each case is printed before it
 runs, and every assertion names its case.
 """
 
@@ -15,7 +17,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import dev_i32, dev_i64, say
+from gpu_util import CODE_OF_KIND, dev_i32, dev_i64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +193,54 @@ def test_fuzz_roll(thd):
             assert np.array_equal(mask[k].cpu().numpy(),
                                   O.swap_rows(want_m[k], w.cu_padded, cp, total, "c2z")), f"{tag} mask {k}"
         route.close()
+
+
+def test_fuzz_pack(thd):
+    import torch
+    pad, eod = 0, 1
+    codes = dict(CODE_OF_KIND, PACK_DOCS=thd.THD_ERR_PACK_DOCS, PACK_CAPACITY=thd.THD_ERR_PACK_CAPACITY)
+    rng = np.random.default_rng([W.BASE_SEED, 940])
+    for case in range(120):
+        batch = int(rng.integers(1, 41))
+        seq = int(rng.integers(1, min(5000, 40000 // batch) + 1))
+        eod_rate = float(rng.choice([0.0, 0.001, 0.01, 0.05, 0.3]))
+        tail = [None, 0, 1, 10, seq][int(rng.integers(0, 5))]
+        inner = float(rng.choice([0.0, 0.01, 0.1]))
+        align = int(rng.choice([1, 2, 3, 4, 8, 16, 64, 512]))
+        rows = W.token_rows([941, case], batch, seq, pad, eod, eod_rate, tail, inner)
+        # the budget is a host-side choice, sized from the oracle's documents
+        _, cu_r, _ = O.pack_batch(rows, pad, eod, 1, batch * seq, batch * seq + 1, 0)
+        lengths = np.diff(cu_r.astype(np.int64))
+        n_docs = int(np.count_nonzero(lengths > 0))
+        used = int(sum(n + (-n) % align for n in lengths[:n_docs]))
+        kind = rng.choice(["fits", "fits", "fits", "docs", "capacity", "both"])
+        capacity = used + align * int(rng.choice([0, 1, 7]))
+        max_docs = n_docs + int(rng.choice([0, 1, 5]))
+        if kind in ("docs", "both") and n_docs > 0:
+            max_docs = n_docs - 1
+        if kind in ("capacity", "both") and used >= align:
+            capacity = used - align * int(rng.integers(1, min(3, used // align) + 1))
+        fill = int(rng.integers(-5, 5))
+        tag = f"pack case {case}: [{batch}, {seq}] eod {eod_rate} align {align} docs {n_docs} used {used} " \
+              f"capacity {capacity} max_docs {max_docs}"
+        say(tag)
+        try:
+            want, want_code = O.pack_batch(rows, pad, eod, align, capacity, max_docs, fill), 0
+        except O.OracleInputError as e:
+            want, want_code = None, codes[e.kind]
+        nbytes = thd.thd_pack_workspace_bytes(batch, seq)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        packed = torch.full((capacity,), -7, dtype=torch.int64, device="cuda")
+        cu_real = torch.full((max_docs + 2,), -7, dtype=torch.int32, device="cuda")
+        cu_pad = torch.full((max_docs + 2,), -7, dtype=torch.int32, device="cuda")
+        status = torch.full((1,), 99, dtype=torch.int32, device="cuda")
+        assert thd.thd_pack(dev_i64(rows), batch, seq, pad, eod, align, capacity, max_docs, fill, ws, nbytes, packed,
+                            cu_real, cu_pad, status) == thd.THD_OK, tag
+        torch.cuda.synchronize()
+        assert int(status.item()) == want_code, tag
+        if want is None:
+            assert (packed == -7).all() and (cu_real == -7).all() and (cu_pad == -7).all(), tag
+        else:
+            assert np.array_equal(packed.cpu().numpy(), want[0]), tag
+            assert np.array_equal(cu_real.cpu().numpy(), want[1]), tag
+            assert np.array_equal(cu_pad.cpu().numpy(), want[2]), tag
