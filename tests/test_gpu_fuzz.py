@@ -8,7 +8,7 @@ under random launch-shape overrides (tile size, workgroup cap, cache policy,
 block size, tile order); several tensors through one launch; label rolls with
 real lengths shorter than the padded ones, in natural and in zigzag order;
 packs of token rows with budgets that fit, that hold too few documents, too
-few tokens, or both.  Each case is printed before it
+few tokens, or both; corrupted boundary lists on every route-build path.  Each case is printed before it
 runs, and every assertion names its case.
 """
 
@@ -244,3 +244,56 @@ def test_fuzz_pack(thd):
             assert np.array_equal(packed.cpu().numpy(), want[0]), tag
             assert np.array_equal(cu_real.cpu().numpy(), want[1]), tag
             assert np.array_equal(cu_pad.cpu().numpy(), want[2]), tag
+
+
+def test_fuzz_bad_boundaries(thd):
+    # one to three corruptions of a valid boundary list (first boundary,
+    # a decrease, the total, a length off the 2*cp grid), with slot counts that
+    # take each build path (one launch, one workgroup in LDS, one workgroup in
+    # global memory): the status is the oracle's first failing rule and no
+    # swap writes anything
+    import torch
+    rng = np.random.default_rng([W.BASE_SEED, 950])
+    for case in range(60):
+        cp = int(rng.choice([2, 3, 4, 8, 16, 64]))
+        n_docs = int(rng.choice([3, 100, 1500, 14000]))
+        max_chunk = max(1, min(8, 120000 // (2 * cp * n_docs)))
+        w = W.random_packed([951, case], cp, n_docs, max_chunk, int(rng.integers(0, 4)), row_shape=(1,),
+                            row_dtype="uint8")
+        cu = w.cu_padded.astype(np.int64).copy()
+        total = int(cu[-1])
+        n = len(cu) - 1
+        kinds = rng.choice(["start", "monotone", "total", "divisible"], size=int(rng.integers(1, 4)), replace=False)
+        for kind in kinds:
+            if kind == "start":
+                cu[0] = int(rng.choice([-3, -1, 1, 2, 2 * cp]))
+            elif kind == "monotone" and n >= 2:
+                i = int(rng.integers(1, n))
+                cu[i] = cu[i - 1] - int(rng.integers(1, 10))
+            elif kind == "total":
+                total += 2 * cp * int(rng.integers(1, 4))
+            elif kind == "divisible":
+                room = [i for i in range(1, n) if cu[i + 1] - cu[i] >= 2 * cp and cu[i] >= cu[i - 1]]
+                if room:
+                    i = room[int(rng.integers(0, len(room)))]
+                    cu[i] += int(rng.integers(1, 2 * cp))
+        try:
+            O.build_route(cu.tolist(), cp, total)
+            continue                               # the corruptions cancelled out: nothing to check
+        except O.OracleInputError as e:
+            rule = e.kind
+        want = CODE_OF_KIND[rule]
+        tag = f"bad boundaries case {case}: cp {cp} slots {n} T {total} corruptions {list(kinds)} -> {rule}"
+        say(tag)
+        route = thd.Route(n, cp, total)
+        route.build(dev_i32(cu), cp, total)
+        assert route.status() == want, tag
+        x = torch.arange(total * 4, dtype=torch.int32, device="cuda").view(total, 4)
+        out = torch.full_like(x, -77)
+        for d in (thd.Z2C, thd.C2Z):
+            assert thd.thd_swap(route.handle, d, x, out, total, 16) == thd.THD_OK, tag
+        torch.cuda.synchronize()
+        assert (out == -77).all(), tag
+        by_src, _, _ = route.copy_out()
+        assert by_src.shape[0] == 0, tag
+        route.close()
