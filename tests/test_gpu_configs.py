@@ -206,6 +206,46 @@ def test_maximum_size_swap_wide_rows(thd):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("rb", [3, 12])
+def test_maximum_size_swap_narrow_rows(thd, rb):
+    # T = 2**31 - 64 tokens of 3- and 12-byte rows (1- and 4-byte copy units,
+    # run pieces realigned onto 16-byte stores): 6 and 24 GiB per buffer, so
+    # the realigning copy runs at byte offsets past 2**32.  Sampled rows
+    # against the oracle's single-token form, every run's first and last
+    # token included; then the round trip.
+    import torch
+    cp = 4
+    total = 2 ** 31 - 64
+    lens = [8, 1 << 30, 16, 536870912, 24, total - (1 << 30) - 536870912 - 48]
+    assert all(v % (2 * cp) == 0 for v in lens) and sum(lens) == total
+    cu = W.cumulative(lens)
+    say("maximum size, narrow rows", rb, total)
+    route = thd.Route(len(lens), cp, total)
+    route.build(dev_i32(cu), cp, total)
+    assert route.status() == 0
+    by_src, _, _ = route.copy_out()
+    g = torch.Generator(device="cuda").manual_seed(W.BASE_SEED + 43 + rb)
+    x = torch.empty((total, rb), dtype=torch.uint8, device="cuda")
+    if rb % 4 == 0:
+        x.view(torch.int32).random_(generator=g)
+    else:
+        x.random_(0, 256, generator=g)
+    out = route.swap(x, thd.Z2C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7 + rb)
+    toks = np.unique(np.concatenate([rng.integers(0, total, 3000), by_src[:, 1].astype(np.int64),
+                                     by_src[:, 1].astype(np.int64) + by_src[:, 2] - 1, [0, total - 1]]))
+    src = np.array([O.zigzag_position(cu, cp, total, int(t)) for t in toks], dtype=np.int64)
+    got = out.index_select(0, torch.from_numpy(toks).cuda()).cpu().numpy()
+    want = x.index_select(0, torch.from_numpy(src).cuda()).cpu().numpy()
+    assert np.array_equal(got, want)
+    back = route.swap(out, thd.C2Z)
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    del x, out, back, route
+    torch.cuda.empty_cache()
+
+
 def test_maximum_size_roll(thd):
     # T = 2**31 - 64 positions, two shifts: the label and MTP outputs reach
     # 2 x 16 GiB, so every index past 2**31 is exercised.  Checked at sampled
