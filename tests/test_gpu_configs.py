@@ -246,6 +246,46 @@ def test_maximum_size_swap_narrow_rows(thd, rb):
     torch.cuda.empty_cache()
 
 
+def test_maximum_size_swap_batch(thd):
+    # T = 2**31 - 64 tokens through the multi-tensor swap in one launch: a
+    # uint8 key, 3-byte rows and an int64 key (2, 6 and 16 GiB per buffer).
+    # Sampled rows against the oracle's single-token form, every run's first
+    # and last token included; then the round trip.
+    import torch
+    cp = 4
+    total = 2 ** 31 - 64
+    lens = [16, 1 << 30, 8, 536870912, 24, total - (1 << 30) - 536870912 - 48]
+    assert all(v % (2 * cp) == 0 for v in lens) and sum(lens) == total
+    cu = W.cumulative(lens)
+    say("maximum size, multi-tensor swap", total)
+    route = thd.Route(len(lens), cp, total)
+    route.build(dev_i32(cu), cp, total)
+    assert route.status() == 0
+    by_src, _, _ = route.copy_out()
+    g = torch.Generator(device="cuda").manual_seed(W.BASE_SEED + 47)
+    xs = [torch.empty((total, 1), dtype=torch.uint8, device="cuda"),
+          torch.empty((total, 3), dtype=torch.uint8, device="cuda"),
+          torch.empty((total,), dtype=torch.int64, device="cuda")]
+    xs[0].random_(0, 256, generator=g)
+    xs[1].random_(0, 256, generator=g)
+    xs[2].random_(generator=g)
+    outs = route.swap_many(xs, thd.Z2C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([rng.integers(0, total, 3000), by_src[:, 1].astype(np.int64),
+                                     by_src[:, 1].astype(np.int64) + by_src[:, 2] - 1, [0, total - 1]]))
+    src = np.array([O.zigzag_position(cu, cp, total, int(t)) for t in toks], dtype=np.int64)
+    t_toks, t_src = torch.from_numpy(toks).cuda(), torch.from_numpy(src).cuda()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        assert torch.equal(o.index_select(0, t_toks), x.index_select(0, t_src)), f"tensor {i}"
+    backs = route.swap_many(outs, thd.C2Z)
+    torch.cuda.synchronize()
+    for i, (x, b) in enumerate(zip(xs, backs)):
+        assert torch.equal(b, x), f"tensor {i}"
+    del xs, outs, backs, route
+    torch.cuda.empty_cache()
+
+
 def test_maximum_size_roll(thd):
     # T = 2**31 - 64 positions, two shifts: the label and MTP outputs reach
     # 2 x 16 GiB, so every index past 2**31 is exercised.  Checked at sampled
