@@ -46,6 +46,7 @@ from .thd_oracle import (  # noqa: F401
     build_route,
     canonical_runs,
     swap_rows,
+    apply_route,
     roll_labels,
     roll_valid_at,
     pack_batch,

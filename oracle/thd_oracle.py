@@ -271,22 +271,43 @@ def swap_rows(x: np.ndarray, cu, cp: int, total: int, direction: str) -> np.ndar
     ``"c2z"``.  Row ``j`` of the output holds the token that the target layout
     puts there, copied bit for bit from the row that holds it in the source
     layout.  cp == 1 returns ``x`` itself (the identity, Relax PR #273 §2.2).
+    The route is built, then applied: ``build_route`` followed by
+    ``apply_route``.
     """
     if direction not in ("z2c", "c2z"):
         raise OracleInputError("DIRECTION", f"unknown direction {direction!r}")
     x = np.asarray(x)
     if x.shape[0] != total:
         raise OracleInputError("SHAPE", f"x has {x.shape[0]} rows, route has {total}")
-    route = build_route(cu, cp, total)
-    if cp == 1 or total == 0:
-        return x
+    return apply_route(x, build_route(cu, cp, total), direction)
+
+
+def apply_route(x: np.ndarray, route: dict, direction: str, out_rows=None) -> np.ndarray:
+    """Apply a route from ``build_route`` to the rows of ``x`` (the swap
+    alone, without building the route).
+
+    ``out_rows`` (a ``slice`` of output rows, default all) produces only those
+    rows of the output, so a batch too large to gather at once can be checked
+    piece by piece; the result then has ``len(range(total)[out_rows])`` rows.
+    An identity route returns ``x`` (or its rows ``out_rows``) itself.
+    """
+    if direction not in ("z2c", "c2z"):
+        raise OracleInputError("DIRECTION", f"unknown direction {direction!r}")
+    x = np.asarray(x)
+    total = route["total"]
+    if x.shape[0] != total:
+        raise OracleInputError("SHAPE", f"x has {x.shape[0]} rows, route has {total}")
+    if route["cp"] == 1 or total == 0:
+        return x if out_rows is None else x[out_rows]
     raw = x.reshape(total, -1).view(np.uint8) if x.size else x.reshape(total, 0).view(np.uint8)
     if direction == "z2c":
         source_of_out = route["src_row"][route["contiguous"]]
     else:
         source_of_out = route["dst_row"][route["zigzag"]]
+    if out_rows is not None:
+        source_of_out = source_of_out[out_rows]
     out = np.take(raw, source_of_out, axis=0)
-    return out.view(x.dtype).reshape(x.shape)
+    return out.view(x.dtype).reshape((out.shape[0],) + x.shape[1:])
 
 
 # ---------------------------------------------------------------------------

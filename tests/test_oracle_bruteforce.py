@@ -205,6 +205,27 @@ def test_emulated_all_to_all_matches_global_swap(seed):
     assert np.array_equal(out, O.swap_rows(zig, cu, cp, total, "z2c"))
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_route_applied_piece_by_piece_equals_the_whole_swap(seed):
+    # Applying a built route to slices of output rows and stacking them gives
+    # the one-shot swap (the form used to check batches too large to gather
+    # at once); the route is built once and applied in both directions.
+    cp = [2, 3, 4, 8][seed]
+    w = W.random_packed(40 + seed, cp, n_docs=6 + seed, max_chunk=7, n_empty=seed % 2)
+    cu, total = w.cu_padded.tolist(), w.total
+    route = O.build_route(cu, cp, total)
+    x = w.rows_host()
+    for direction in ("z2c", "c2z"):
+        whole = O.swap_rows(x, cu, cp, total, direction)
+        assert np.array_equal(O.apply_route(x, route, direction), whole)
+        step = max(1, total // 5 + 1)
+        pieces = [O.apply_route(x, route, direction, slice(a, min(a + step, total))) for a in range(0, total, step)]
+        assert np.array_equal(np.concatenate(pieces), whole)
+    # an identity route hands the input back
+    one = O.build_route(cu, 1, total)
+    assert O.apply_route(x, one, "z2c") is x
+
+
 def test_roll_matches_per_document_numpy_roll():
     # Unpadded documents: shift j inside a document is np.roll(doc, -j) with the
     # last j positions cleared.

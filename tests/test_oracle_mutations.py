@@ -63,6 +63,15 @@ def _swap_directions_exchanged(x, cu, cp, total, direction):
     return _real_swap(x, cu, cp, total, other)
 
 
+_real_apply = T.apply_route
+
+
+def _apply_gathers_by_the_inverse(x, route, direction, out_rows=None):
+    # gathers with the row list of the other direction (the inverse permutation)
+    other = {"z2c": "c2z", "c2z": "z2c"}.get(direction, direction)
+    return _real_apply(x, route, other, out_rows)
+
+
 _real_roll = T.roll_labels
 
 
@@ -150,6 +159,7 @@ MUTATIONS = {
     "chunks of L/cp": ("zigzag_rank_tokens", _zig_chunk_by_cp),
     "contiguous ranks reversed": ("contiguous_rank_tokens", _contig_reversed),
     "swap directions exchanged": ("swap_rows", _swap_directions_exchanged),
+    "route applied by its inverse": ("apply_route", _apply_gathers_by_the_inverse),
     "roll ignores real lengths": ("roll_labels", _roll_uses_padded_end),
     "label crosses the document end": ("roll_labels", _roll_off_by_one),
     "monotone check dropped": ("check_route_boundaries", _check_monotone_skipped),
