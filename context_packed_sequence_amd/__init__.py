@@ -54,8 +54,8 @@ from .binding import (  # noqa: F401
     thd_route_status,
     thd_strerror,
     thd_swap,
+    thd_route_launch_shape,
     thd_swap_batch,
-    thd_swap_tuning,
 )
 
 Z2C = THD_ZIGZAG_TO_CONTIGUOUS

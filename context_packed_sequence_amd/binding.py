@@ -49,9 +49,9 @@ THD_PACK_MAX_SEQ = 2147479552
 
 EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",
-    "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_swap_tuning", "thd_strerror",
+    "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_strerror",
     "thd_swap_batch", "thd_roll_labels_zigzag", "thd_pack_workspace_bytes", "thd_pack", "thd_copy",
-    "thd_read_stream", "thd_write_stream",
+    "thd_route_launch_shape", "thd_read_stream", "thd_write_stream",
 )
 
 
@@ -78,7 +78,6 @@ def _load() -> ctypes.CDLL:
         "thd_route_copy_out": (ctypes.c_int, [c_p, c_p, ctypes.POINTER(c_i32), c_i32, c_p, c_p, c_p]),
         "thd_route_info": (ctypes.c_int, [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i64),
                                           ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]),
-        "thd_swap_tuning": (ctypes.c_int, [c_i64, c_i32, c_i32, c_i32, c_i32]),
         "thd_strerror": (ctypes.c_char_p, [c_i32]),
         "thd_swap_batch": (ctypes.c_int, [c_p, c_i32, c_i32, ctypes.POINTER(c_p), ctypes.POINTER(c_p),
                                           ctypes.POINTER(c_i64), c_i64, c_p]),
@@ -86,6 +85,7 @@ def _load() -> ctypes.CDLL:
                                                   c_p]),
         "thd_pack_workspace_bytes": (ctypes.c_int64, [c_i32, c_i32]),
         "thd_copy": (ctypes.c_int, [c_p, c_p, c_i64, c_p]),
+        "thd_route_launch_shape": (ctypes.c_int, [c_p, c_i64, c_i32, c_i32, c_i32]),
         "thd_read_stream": (ctypes.c_int, [c_p, c_i64, c_p, c_p, c_p]),
         "thd_write_stream": (ctypes.c_int, [c_p, c_i64, ctypes.c_uint32, c_p]),
         "thd_pack": (ctypes.c_int, [c_p, c_i32, c_i32, c_i64, c_i64, c_i32, c_i64, c_i32, c_i64, c_p, c_i64, c_p,
@@ -239,11 +239,12 @@ def thd_route_info(route: int) -> dict:
     return {"cp_size": cp.value, "total_tokens": total.value, "n_slots": n_slots.value, "built": bool(built.value)}
 
 
-def thd_swap_tuning(tile_bytes: int = 0, max_workgroups: int = 0, nontemporal: int = 1,
-                    block_threads: int = 0, tile_order: int = 0) -> None:
-    """Override the swap launch shape (0 = built-in choice); no arguments restore the defaults."""
-    _check(_lib.thd_swap_tuning(tile_bytes, max_workgroups, nontemporal, block_threads, tile_order),
-           "thd_swap_tuning")
+def thd_route_launch_shape(route: int, tile_bytes: int = 0, nontemporal: int = 1, block_threads: int = 0,
+                           tile_order: int = 0) -> None:
+    """Override the launch shape of later swaps on one route (0 = built-in
+    choice); no shape arguments restore the defaults (include/thd_cp_bench.h)."""
+    _check(_lib.thd_route_launch_shape(route, tile_bytes, nontemporal, block_threads, tile_order),
+           "thd_route_launch_shape")
 
 
 def library():

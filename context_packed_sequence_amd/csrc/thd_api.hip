@@ -8,6 +8,7 @@
 #include <new>
 #include <vector>
 
+#include "thd_cp_bench.h"
 #include "thd_internal.h"
 
 using thdcp::RouteDev;
@@ -27,11 +28,11 @@ struct thd_route {
   int32_t cp = 0;
   int64_t total = 0;
   int32_t n_slots = 0;
+  // launch-shape override of this route's swaps (thd_route_launch_shape)
+  thdcp::SwapLaunch launch{0, 1, 0, 0};
 };
 
 namespace {
-
-thdcp::SwapLaunch g_swap_cfg{0, 0, 1, 0, 0};
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -198,7 +199,7 @@ int thd_swap(const thd_route* route, int32_t direction, const void* in, void* ou
   const thdcp::DirEntry* dir = z2c ? route->dev.dir_dst : route->dev.dir_src;
   const int word = z2c ? thdcp::kHdrRunsDst : thdcp::kHdrRunsSrc;
   if (thdcp::launch_swap(route->dev.hdr, runs, word, dir, in, out, static_cast<int32_t>(rows), row_bytes,
-                         typical_run_rows(route), g_swap_cfg, as_stream(stream)) != hipSuccess)
+                         typical_run_rows(route), route->launch, as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;
   return THD_OK;
 }
@@ -208,7 +209,7 @@ int thd_copy(const void* in, void* out, int64_t bytes, void* stream) {
   if (bytes == 0) return THD_OK;
   if (!in || !out) return THD_ERR_ARG;
   if (overlaps(in, bytes, out, bytes)) return THD_ERR_ALIAS;
-  if (thdcp::launch_copy(in, out, bytes, g_swap_cfg, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
+  if (thdcp::launch_copy(in, out, bytes, as_stream(stream)) != hipSuccess) return THD_ERR_HIP;
   return THD_OK;
 }
 
@@ -439,14 +440,13 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
   return THD_OK;
 }
 
-int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
-                    int32_t tile_order) {
-  if (tile_bytes < 0 || max_workgroups < 0 || nontemporal < 0 || nontemporal > 1 || tile_order < 0)
-    return THD_ERR_ARG;
+int thd_route_launch_shape(thd_route* route, int64_t tile_bytes, int32_t nontemporal, int32_t block_threads,
+                           int32_t tile_order) {
+  if (!route || tile_bytes < 0 || nontemporal < 0 || nontemporal > 1 || tile_order < 0) return THD_ERR_ARG;
   if (block_threads != 0 && block_threads != 128 && block_threads != 256 && block_threads != 512 &&
       block_threads != 1024)
     return THD_ERR_ARG;
-  g_swap_cfg = thdcp::SwapLaunch{tile_bytes, max_workgroups, nontemporal, block_threads, tile_order};
+  route->launch = thdcp::SwapLaunch{tile_bytes, nontemporal, block_threads, tile_order};
   return THD_OK;
 }
 

@@ -70,17 +70,16 @@ hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t str
 // launch_route_index must not follow it.
 bool route_build_fused(int32_t n_slots, int32_t cp);
 
-// Swap launch overrides; 0 in a field means the built-in choice.
+// Swap launch overrides of one route; 0 in a field means the built-in choice.
 struct SwapLaunch {
   int64_t tile_bytes;
-  int32_t max_workgroups;
   int32_t nontemporal;    // 1 on, 0 off
   int32_t block_threads;  // 128, 256, 512 or 1024
   int32_t tile_order;     // tiles per XCD chunk: 1 natural order, G > 1 XCD-chunked
 };
 
-// Plain streaming copy (thd_copy); cfg.block_threads and cfg.tile_order apply.
-hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunch& cfg, hipStream_t stream);
+// Plain streaming copy (thd_copy) in its own fixed shape.
+hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t stream);
 hipError_t launch_read_stream(const void* in, int64_t bytes, const uint32_t key[4], uint32_t* count,
                               hipStream_t stream);
 hipError_t launch_write_stream(void* out, int64_t bytes, uint32_t seed, hipStream_t stream);

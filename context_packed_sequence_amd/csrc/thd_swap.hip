@@ -145,9 +145,9 @@ __device__ __forceinline__ void copy_bytes_realigned(const unsigned char* __rest
 // realigning copy.
 constexpr int64_t kRealignMinBytes = 256;
 
-// One tile of output rows [r0, r1): find the run holding r0 from the
-// directory (one 16-byte load covers the usual case where no run starts
-// between the directory row, a multiple of 16, and r0; otherwise the entry's
+// One tile of output rows [r0, r1): find the run holding r0 from e, the
+// directory entry of r0's 16-row block (it alone covers the usual case where
+// no run starts between the block's first row and r0; otherwise the entry's
 // run-start bits name the run, and one load of it follows), then copy run
 // piece by run piece.  Every access stays inside the run table and inside
 // [0, total) rows of both buffers.
@@ -155,11 +155,9 @@ constexpr int64_t kRealignMinBytes = 256;
 // source words per output word, so half a plain copy's unroll keeps the
 // registers in flight the same); 0 leaves narrow units to the plain copy.
 template <typename U, int BLOCK, int UNROLL, bool NT, int PAIRS = (UNROLL > 2 ? UNROLL / 2 : 1)>
-__device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
-                                          int32_t n_runs, const unsigned char* __restrict__ in,
-                                          unsigned char* __restrict__ out, int32_t total, int64_t row_bytes,
-                                          int32_t r0, int32_t r1) {
-  const DirEntry e = dir[r0 >> kDirShift];
+__device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, const DirEntry& e, int32_t n_runs,
+                                          const unsigned char* __restrict__ in, unsigned char* __restrict__ out,
+                                          int32_t total, int64_t row_bytes, int32_t r0, int32_t r1) {
   int32_t k, in_row, run_end;
   if (r0 < e.run_end) {
     k = e.run;
@@ -198,13 +196,12 @@ __device__ __forceinline__ void swap_tile(const RunPair* __restrict__ runs, cons
 }
 
 // Part of one output row: bytes [b0, b1) of row r, for rows so long that a
-// workgroup takes a slice of a row rather than whole rows.
+// workgroup takes a slice of a row rather than whole rows; e is the directory
+// entry of r's 16-row block.
 template <typename U, int BLOCK, int UNROLL, bool NT>
-__device__ __forceinline__ void swap_row_part(const RunPair* __restrict__ runs, const DirEntry* __restrict__ dir,
-                                              int32_t n_runs, const unsigned char* __restrict__ in,
-                                              unsigned char* __restrict__ out, int64_t row_bytes, int32_t r,
-                                              int64_t b0, int64_t b1) {
-  const DirEntry e = dir[r >> kDirShift];
+__device__ __forceinline__ void swap_row_part(const RunPair* __restrict__ runs, const DirEntry& e, int32_t n_runs,
+                                              const unsigned char* __restrict__ in, unsigned char* __restrict__ out,
+                                              int64_t row_bytes, int32_t r, int64_t b0, int64_t b1) {
   int32_t in_row;
   if (r < e.run_end) {
     in_row = e.in + (r & (kDirBlock - 1));
@@ -271,7 +268,8 @@ __device__ __forceinline__ void swap_tile_small(const RunPair* __restrict__ runs
       if (r < r1) store_unit<NT>(out + r, v[m]);
     }
   } else {
-    swap_tile<U, BLOCK, 8, NT, 0>(runs, dir, n_runs, in8, out8, total, static_cast<int64_t>(sizeof(U)), r0, r1);
+    swap_tile<U, BLOCK, 8, NT, 0>(runs, dir[r0 >> kDirShift], n_runs, in8, out8, total,
+                                  static_cast<int64_t>(sizeof(U)), r0, r1);
   }
   __syncthreads();  // the next tile reuses s_runs and s_k
 }
@@ -302,8 +300,24 @@ __global__ __launch_bounds__(BLOCK) void swap_small_kernel(const int32_t* __rest
 // back, i.e. workgroup b = 8 j + x copies tile ((j / G) * 8 + x) * G + j mod G.
 constexpr int kXcds = 8;
 
-// Capped at 64 VGPRs (8 waves per SIMD); the 16-byte-unit kernels need under
-// 50, the narrow ones 63-64 with no spills.
+__device__ __forceinline__ int32_t tile_of_slot(int32_t slot, int32_t chunk) {
+  const int32_t x = slot % kXcds, j = slot / kXcds;
+  return chunk == 1 ? slot : ((j / chunk) * kXcds + x) * chunk + j % chunk;
+}
+
+// One tile per workgroup.  Capped at 64 VGPRs (8 waves per SIMD); the
+// 16-byte-unit kernels need under 50, the narrow ones 63-64 with no spills.
+//
+// A workgroup lives a few microseconds and moves a few KiB, so the memory
+// round trips before its first data load are a visible share of its life.
+// The route's status word, its run count and the directory entry of the
+// tile's first row do not depend on each other and are read in one round
+// trip: the empty asm statement takes all three as operands before the
+// status test, so no load can sink below the test.  The entry's address lies
+// inside the directory whatever the status; its value is used only once the
+// status is good.  (Measured on MI355X: 0.6-1.2 % on 4 KiB rows against
+// reading the status first.  The same reads inside a loop over several tiles
+// per workgroup cost 5 %, so the kernel takes exactly one.)
 template <typename U, int BLOCK, int UNROLL, bool NT>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void swap_kernel(const int32_t* __restrict__ hdr, int runs_word,
                                                      const RunPair* __restrict__ runs,
@@ -311,23 +325,22 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
                                                      const unsigned char* __restrict__ in,
                                                      unsigned char* __restrict__ out, int32_t total,
                                                      int64_t row_bytes, int32_t tile_rows, int32_t n_tiles,
-                                                     int32_t chunk, int32_t n_slots, int32_t parts,
-                                                     int64_t part_bytes) {
-  if (hdr[kHdrStatus] != THD_OK) return;  // a failed build writes nothing
+                                                     int32_t chunk, int32_t parts, int64_t part_bytes) {
+  const int32_t tile = tile_of_slot(blockIdx.x, chunk);
+  if (tile >= n_tiles) return;
+  // first output row of the tile (rows cut into slices: tile = (row, slice))
+  const int32_t r = parts > 1 ? tile / parts : tile * tile_rows;
+  const int32_t status = hdr[kHdrStatus];
   const int32_t n_runs = hdr[runs_word];
-  for (int32_t slot = blockIdx.x; slot < n_slots; slot += gridDim.x) {
-    const int32_t x = slot % kXcds, j = slot / kXcds;
-    const int32_t tile = chunk == 1 ? slot : ((j / chunk) * kXcds + x) * chunk + j % chunk;
-    if (tile >= n_tiles) continue;
-    if (parts > 1) {  // rows cut into slices: tile = (row, slice)
-      const int32_t r = tile / parts;
-      const int64_t b0 = static_cast<int64_t>(tile - r * parts) * part_bytes;
-      swap_row_part<U, BLOCK, UNROLL, NT>(runs, dir, n_runs, in, out, row_bytes, r, b0, min(row_bytes, b0 + part_bytes));
-      continue;
-    }
-    const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(tile) * tile_rows);
-    const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + tile_rows));
-    swap_tile<U, BLOCK, UNROLL, NT>(runs, dir, n_runs, in, out, total, row_bytes, r0, r1);
+  const DirEntry e = dir[r >> kDirShift];
+  asm volatile("" ::"s"(status), "s"(n_runs), "s"(e.in), "s"(e.run_end), "s"(e.run), "s"(e.starts));
+  if (status != THD_OK) return;  // a failed build writes nothing
+  if (parts > 1) {
+    const int64_t b0 = static_cast<int64_t>(tile - r * parts) * part_bytes;
+    swap_row_part<U, BLOCK, UNROLL, NT>(runs, e, n_runs, in, out, row_bytes, r, b0, min(row_bytes, b0 + part_bytes));
+  } else {
+    const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r) + tile_rows));
+    swap_tile<U, BLOCK, UNROLL, NT>(runs, e, n_runs, in, out, total, row_bytes, r, r1);
   }
 }
 
@@ -366,8 +379,7 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
   if (hdr[kHdrStatus] != THD_OK) return;
   const int32_t n_runs = hdr[runs_word];
   for (int32_t slot = blockIdx.x; slot < args.n_slots; slot += gridDim.x) {
-    const int32_t x = slot % kXcds, j = slot / kXcds;
-    const int32_t g = args.chunk == 1 ? slot : ((j / args.chunk) * kXcds + x) * args.chunk + j % args.chunk;
+    const int32_t g = tile_of_slot(slot, args.chunk);
     if (g >= args.total_tiles) continue;
     int i = 0;
     while (i + 1 < args.n && args.t[i + 1].first_tile <= g) ++i;
@@ -376,7 +388,8 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
       const int32_t r = (g - bt.first_tile) / bt.parts;
       const int64_t b0 = static_cast<int64_t>((g - bt.first_tile) % bt.parts) * bt.part_bytes;
       const int64_t b1 = min(bt.row_bytes, b0 + bt.part_bytes);
-      swap_row_part<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, bt.row_bytes, r, b0, b1);
+      swap_row_part<u32x4, kBatchBlock, 8, true>(runs, dir[r >> kDirShift], n_runs, bt.in, bt.out, bt.row_bytes, r,
+                                                 b0, b1);
       continue;
     }
     const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(g - bt.first_tile) * bt.tile_rows);
@@ -390,12 +403,13 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
       }
       continue;
     }
+    const DirEntry& e = dir[r0 >> kDirShift];
     switch (bt.unit) {
-      case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 8: swap_tile<u32x2, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 4: swap_tile<uint32_t, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 2: swap_tile<uint16_t, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      default: swap_tile<uint8_t, kBatchBlock, 8, true, 0>(runs, dir, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 8: swap_tile<u32x2, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 4: swap_tile<uint32_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 2: swap_tile<uint16_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      default: swap_tile<uint8_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
     }
   }
 }
@@ -403,15 +417,12 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
 // Plain streaming copy of 4 KiB tiles: no route, no permutation.  The swap's
 // units, tiles and non-temporal accesses; 128 threads in XCD-chunked order
 // with chunks of 256 tiles, the fastest plain-copy shape in sweeps on
-// MI355X (the swap's workgroup size and tile order from thd_swap_tuning
-// apply here too, for sweeps).
+// MI355X.
 template <typename U, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void copy_kernel(const unsigned char* __restrict__ in,
                                                      unsigned char* __restrict__ out, int64_t bytes,
                                                      int64_t tile_bytes, int32_t n_tiles, int32_t chunk) {
-  const int32_t slot = blockIdx.x;
-  const int32_t x = slot % kXcds, j = slot / kXcds;
-  const int32_t tile = chunk == 1 ? slot : ((j / chunk) * kXcds + x) * chunk + j % chunk;
+  const int32_t tile = tile_of_slot(blockIdx.x, chunk);
   if (tile >= n_tiles) return;
   const int64_t b0 = static_cast<int64_t>(tile) * tile_bytes;
   const int64_t n = min(tile_bytes, bytes - b0) / static_cast<int64_t>(sizeof(U));
@@ -444,7 +455,7 @@ int copy_unit(int64_t row_bytes, const void* in, const void* out) {
 }
 
 struct Shape {
-  int32_t tile_rows, n_tiles, chunk, n_slots, grid, parts;
+  int32_t tile_rows, n_tiles, chunk, grid, parts;
   int64_t part_bytes;
 };
 
@@ -455,11 +466,11 @@ hipError_t launch_typed(const int32_t* hdr, const RunPair* runs, int runs_word, 
   auto* o8 = static_cast<unsigned char*>(out);
   if (nt)
     hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, true>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr, runs_word,
-                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots, sh.parts,
+                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.parts,
                        sh.part_bytes);
   else
     hipLaunchKernelGGL((swap_kernel<U, BLOCK, UNROLL, false>), dim3(sh.grid), dim3(BLOCK), 0, stream, hdr, runs_word,
-                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.n_slots, sh.parts,
+                       runs, dir, i8, o8, total, row_bytes, sh.tile_rows, sh.n_tiles, sh.chunk, sh.parts,
                        sh.part_bytes);
   return hipGetLastError();
 }
@@ -484,8 +495,7 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
     constexpr int kBlock = 256;
     const int64_t tiles = (static_cast<int64_t>(total) + kBlock * kSmallRowsPerThread - 1) /
                           (kBlock * kSmallRowsPerThread);
-    int32_t grid = static_cast<int32_t>(tiles);
-    if (cfg.max_workgroups > 0 && grid > cfg.max_workgroups) grid = cfg.max_workgroups;
+    const int32_t grid = static_cast<int32_t>(tiles);
     if (grid <= 0) return hipSuccess;
     const auto* i8 = static_cast<const unsigned char*>(in);
     auto* o8 = static_cast<unsigned char*>(out);
@@ -507,13 +517,15 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   // Launch shape.  Measured on MI355X (head-to-head sweeps on one box,
   // repeated on a second): with 16-byte units every workgroup moves about
   // 4 KiB.  Rows of 4 KiB up to 8 KiB: one row per 256-thread workgroup,
-  // XCD-chunked order with chunks of 128 tiles.  Rows of 8 KiB and more:
+  // XCD-chunked order with chunks of 256 tiles (0.6-1 % over chunks of 128
+  // since the status, run count and directory reads share one round trip).
+  // Rows of 8 KiB and more:
   // 4 KiB slices of one row (whole 128-byte lines where the row is made of
   // them) per 128-thread workgroup, chunks of 64.  Rows of 1-4 KiB: see
   // below.  Shorter rows: 4 KiB tiles of whole rows, 128 threads, natural
   // order.  Units under 16 bytes: 256 threads, 8 KiB tiles, chunks of 64.
-  // Every field can be overridden for sweeps; a tile size below the row
-  // size cuts rows into slices.
+  // Every field can be overridden per route for sweeps; a tile size below
+  // the row size cuts rows into slices.
   const bool big_rows = unit == 16 && row_bytes >= 8192;
   const bool mid_rows = unit == 16 && row_bytes >= 4096 && !big_rows;
   // rows between 1 and 4 KiB that are not powers of two: rows of whole
@@ -530,7 +542,7 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
                                           : (unit == 16 ? (mid_rows || kib_lines ? 256 : 128) : 256);
   int64_t chunk = cfg.tile_order > 0
                       ? cfg.tile_order
-                      : (kib_rows ? (kib_lines ? 128 : 64) : (big_rows ? 64 : (mid_rows ? 128 : (unit == 16 ? 1 : 64))));
+                      : (kib_rows ? (kib_lines ? 128 : 64) : (big_rows ? 64 : (mid_rows ? 256 : (unit == 16 ? 1 : 64))));
 
   int64_t tile_rows = cfg.tile_bytes == 0 && !mid_rows && !big_rows && !kib_rows
                           ? whole_row_tile(row_bytes, tile_bytes)
@@ -558,9 +570,7 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   sh.chunk = static_cast<int32_t>(chunk);
   const int64_t slots = chunk == 1 ? sh.n_tiles : (sh.n_tiles + kXcds * chunk - 1) / (kXcds * chunk) * kXcds * chunk;
   if (slots > INT32_MAX) return hipErrorInvalidValue;
-  sh.n_slots = static_cast<int32_t>(slots);
-  sh.grid = sh.n_slots;
-  if (cfg.max_workgroups > 0 && sh.grid > cfg.max_workgroups) sh.grid = cfg.max_workgroups;
+  sh.grid = static_cast<int32_t>(slots);
   if (sh.grid <= 0) return hipSuccess;
   const bool nt = cfg.nontemporal != 0;
 #define THD_SWAP_ARGS hdr, runs, runs_word, dir, in, out, total, row_bytes, sh, nt, stream
@@ -634,14 +644,14 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
   return hipGetLastError();
 }
 
-hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunch& cfg, hipStream_t stream) {
+hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t stream) {
   const int unit = copy_unit(bytes, in, out);
   const int64_t tile_bytes = unit == 16 ? 4096 : 8192;
   const int64_t tiles = (bytes + tile_bytes - 1) / tile_bytes;
   if (tiles <= 0) return hipSuccess;
   if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
   const int32_t n_tiles = static_cast<int32_t>(tiles);
-  int32_t chunk = cfg.tile_order > 0 ? min(cfg.tile_order, static_cast<int32_t>(INT32_MAX / 16)) : (unit == 16 ? 256 : 1);
+  int32_t chunk = unit == 16 ? 256 : 1;
   const int32_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
   if (chunk > per_xcd) chunk = per_xcd;
   const int64_t slots =
@@ -650,18 +660,10 @@ hipError_t launch_copy(const void* in, void* out, int64_t bytes, const SwapLaunc
   const auto* i8 = static_cast<const unsigned char*>(in);
   auto* o8 = static_cast<unsigned char*>(out);
   const dim3 grid(static_cast<unsigned>(slots));
-  const int block = unit == 16 && cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? 128 : 256);
 #define THD_COPY(U_, B_, R_) \
   hipLaunchKernelGGL((copy_kernel<U_, B_, R_>), grid, dim3(B_), 0, stream, i8, o8, bytes, tile_bytes, n_tiles, chunk)
   switch (unit) {
-    case 16:
-      switch (block) {
-        case 256: THD_COPY(u32x4, 256, 4); break;
-        case 512: THD_COPY(u32x4, 512, 2); break;
-        case 1024: THD_COPY(u32x4, 1024, 2); break;
-        default: THD_COPY(u32x4, 128, 8); break;
-      }
-      break;
+    case 16: THD_COPY(u32x4, 128, 8); break;
     case 8: THD_COPY(u32x2, 256, 4); break;
     case 4: THD_COPY(uint32_t, 256, 8); break;
     case 2: THD_COPY(uint16_t, 256, 8); break;

@@ -292,77 +292,18 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
                    int32_t* n_slots, int32_t* built);
 
 /*
- * thd_swap_tuning -- override the swap kernel's launch shape for later calls
- * in this process (a process-wide setting; not safe to change while another
- * thread calls thd_swap).  For launch-shape sweeps: the results of thd_swap
- * never depend on it.  A 0 selects the built-in choice for that field.  The
- * built-in shapes, for rows moved in 16-byte units: rows under 1 KiB, and
- * 1 KiB and 2 KiB rows, in tiles of about 4 KiB of whole rows (a multiple of
- * 128 bytes where one fits) on 128 threads in natural order; other 1-4 KiB
- * rows made of whole 128-byte lines in tiles of at least 4 KiB on 256
- * threads, chunks of 128; the remaining 1-4 KiB rows one row per 128-thread
- * workgroup, chunks of 64; rows of 4 KiB up to 8 KiB one row per 256-thread
- * workgroup, chunks of 128; rows of 8 KiB and more in slices of about 4 KiB
- * (whole 128-byte lines where the row is made of them) on 128 threads,
- * chunks of 64.  Rows moved in narrower units: 8 KiB tiles on 256 threads,
- * chunks of 64.  Rows of one unit (1-16 B) whose typical run is shorter than
- * one such tile (4 KiB for 16-byte rows) take an LDS-staged kernel instead.
- *   tile_bytes      output bytes per workgroup tile, rounded up to whole rows;
- *                   with 16-byte units, a value below the row size cuts each
- *                   row into slices of about that size
- *   max_workgroups  cap on workgroups; above it workgroups loop over tiles
- *   nontemporal     1: non-temporal loads and stores (built-in), 0: plain
- *   block_threads   128, 256, 512 or 1024; used by the 16-byte path only
- *   tile_order      tiles per XCD chunk: 1 = natural order (tile b to
- *                   workgroup b, so neighbouring tiles go to different
- *                   XCDs); G > 1 = XCD-chunked (tiles cut into chunks of G,
- *                   XCD x streams chunks x, x+8, ...; G >= tiles / 8
- *                   gives each XCD one contiguous eighth)
- * A non-zero tile_bytes or block_threads also sends one-unit rows down the
- * tiled path.  thd_swap_tuning(0, 0, 1, 0, 0) restores the built-in shape.
- */
-int thd_swap_tuning(int64_t tile_bytes, int32_t max_workgroups, int32_t nontemporal, int32_t block_threads,
-                    int32_t tile_order);
-
-/*
  * thd_copy -- plain streaming copy of `bytes` bytes from `in` to `out`
  * (device pointers, non-overlapping): no route, no permutation.  It moves
  * the bytes in 4 KiB tiles with the same 16-byte non-temporal units as
  * thd_swap, in the launch shape that streams a plain copy fastest (128
- * threads per tile, XCD-chunked order with chunks of 256 tiles; the
- * block_threads and tile_order of thd_swap_tuning override it), so a
+ * threads per tile, XCD-chunked order with chunks of 256 tiles), so a
  * swap's bandwidth can be set beside that of a copy of the same bytes in
- * the same run.  Stream-ordered, one launch; THD_ERR_ARG for a
- * negative size or a null pointer (bytes > 0), THD_ERR_ALIAS for overlapping
- * buffers; 0 bytes is THD_OK with no launch.
+ * the same run: the ceiling a row permutation is measured against.
+ * Stream-ordered, one launch; THD_ERR_ARG for a negative size or a null
+ * pointer (bytes > 0), THD_ERR_ALIAS for overlapping buffers; 0 bytes is
+ * THD_OK with no launch.
  */
 int thd_copy(const void* in, void* out, int64_t bytes, void* stream);
-
-/*
- * thd_read_stream / thd_write_stream -- the two streams any row permutation
- * is made of, measured on their own: the swap reads each input byte once and
- * writes each output byte once.  HBM carries reads and writes over the same
- * channels, so a stream that mixes them (a copy, a swap) cannot move bytes
- * faster than a pure read or a pure write stream; these two passes measure
- * the pure streams.  Both use 16-byte non-temporal accesses, 128-thread
- * workgroups and XCD-chunked tile order, in the shapes that streamed fastest
- * on MI355X (4 KiB tiles for the read pass, 2 KiB for the write pass).
- *
- * thd_read_stream reads `bytes` bytes of `in` and adds to *count (device
- * uint32, 4-byte aligned, cleared by the caller) the number of 16-byte words
- * of `in` equal to the 16 bytes at `key` (host).  Only workgroups that find
- * a match touch *count, so with rare matches nothing but reads reach HBM.
- *
- * thd_write_stream writes `bytes` bytes of `out`: 16-byte word w holds four
- * copies of the 32-bit value (uint32)w ^ seed; nothing is read.
- *
- * `bytes` must be a non-negative multiple of 16 and `in` / `out` 16-byte
- * aligned (THD_ERR_ARG otherwise, or for a null pointer with bytes > 0);
- * `count` must not lie inside `in` (THD_ERR_ALIAS).  0 bytes is THD_OK with
- * no launch.  Stream-ordered, one launch each.
- */
-int thd_read_stream(const void* in, int64_t bytes, const void* key, uint32_t* count, void* stream);
-int thd_write_stream(void* out, int64_t bytes, uint32_t seed, void* stream);
 
 /* thd_strerror -- static text for a return or status code. */
 const char* thd_strerror(int32_t code);

@@ -1,4 +1,4 @@
-"""The C-ABI library loads on the host and exports what include/thd_cp.h declares.
+"""The C-ABI library loads on the host and exports what include/*.h declare.
 
 CPU only: nothing here launches a kernel.  The error paths called below are the
 ones the library rejects on the host before any HIP call.
@@ -12,19 +12,23 @@ import pytest
 
 from conftest import ROOT
 
-HEADER = os.path.join(ROOT, "include", "thd_cp.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+
+
+def header_text():
+    return "\n".join(open(h, encoding="utf-8").read() for h in HEADERS)
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"/\*.*?\*/", " ", header_text(), flags=re.S)
     names = re.findall(r"\b(?:int64_t|int|void|const char\s*\*)\s+(thd_[a-z_]+)\s*\(", text)
     return sorted(set(names))
 
 
 def declared_constants():
-    text = open(HEADER, encoding="utf-8").read()
-    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(THD_[A-Z0-9_]+)\s+(-?\d+)", text)}
+    return {m.group(1): int(m.group(2))
+            for m in re.finditer(r"#define\s+(THD_[A-Z0-9_]+)\s+(-?\d+)", header_text())}
 
 
 @pytest.fixture(scope="module")
@@ -120,13 +124,8 @@ def test_host_rejections_without_device_work(pkg):
     assert lib.thd_write_stream((1 << 20) + 4, 16, 0, None) == pkg.THD_ERR_ARG
     assert lib.thd_write_stream(None, 16, 0, None) == pkg.THD_ERR_ARG
     assert lib.thd_write_stream(None, 0, 0, None) == pkg.THD_OK
-    # tuning argument checks
-    assert lib.thd_swap_tuning(-1, 0, 1, 0, 0) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, -1, 1, 0, 0) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, 0, 2, 0, 0) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, 0, 1, 300, 0) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, 0, 1, 0, -1) == pkg.THD_ERR_ARG
-    assert lib.thd_swap_tuning(0, 0, 1, 0, 0) == pkg.THD_OK
+    # the launch-shape override belongs to a route: none given, nothing set
+    assert lib.thd_route_launch_shape(None, 0, 1, 0, 0) == pkg.THD_ERR_ARG
 
 
 def test_package_and_oracle_share_no_code():

@@ -83,52 +83,46 @@ def test_fuzz_swap(thd):
 
 
 TUNE_TILE = [0, 1, 16, 100, 512, 1000, 4096, 5000, 16384, 65536]
-TUNE_WGS = [0, 0, 1, 3, 8, 64, 1000]
 TUNE_BLOCK = [0, 128, 256, 512, 1024]
 TUNE_ORDER = [0, 1, 2, 5, 64, 128, 100000]
 
 
 def test_fuzz_swap_launch_shapes(thd):
-    # every launch-shape override (tile size, workgroup cap, cache policy,
-    # block size, tile order) on rows of any size at byte offsets that force
-    # every copy unit: the result never depends on the shape
+    # every launch-shape override (tile size, cache policy, block size, tile
+    # order) on rows of any size at byte offsets that force every copy unit:
+    # the result never depends on the shape
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 930])
-    try:
-        for case in range(200):
-            cp = int(rng.choice(CPS[1:]))
-            rb = int(rng.choice(ROW_BYTES)) if rng.random() < 0.6 else int(rng.integers(1, 9001))
-            offset = int(rng.choice(OFFSETS + [3, 6, 12]))
-            tune = (int(rng.choice(TUNE_TILE)), int(rng.choice(TUNE_WGS)), int(rng.integers(0, 2)),
-                    int(rng.choice(TUNE_BLOCK)), int(rng.choice(TUNE_ORDER)))
-            budget = 2 << 20 if tune[1] == 0 or tune[1] >= 64 else 192 << 10
-            docs, max_chunk, n_empty = draw_batch(rng, cp, max(1, budget // rb))
-            w = W.random_packed([931, case], cp, docs, max_chunk, n_empty, row_shape=(1,), row_dtype="uint8")
-            total = w.total
-            tag = f"shape case {case}: cp {cp} rb {rb} off {offset} T {total} slots {w.n_slots} tuning {tune}"
-            say(tag)
-            route = thd.Route(max(1, w.n_slots), cp, max(total, 1))
-            route.build(dev_i32(w.cu_padded), cp, total)
-            x_host = np.random.default_rng([932, case]).integers(0, 256, (total, rb), dtype=np.uint8)
-            nbytes = total * rb
-            in_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
-            out_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
-            in_buf[offset:offset + nbytes] = torch.from_numpy(x_host.reshape(-1)).cuda()
-            thd.thd_swap_tuning(*tune)
-            for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
-                out_buf.fill_(0xA5)
-                code = thd.thd_swap(route.handle, d, in_buf.data_ptr() + offset, out_buf.data_ptr() + offset, total,
-                                    rb)
-                torch.cuda.synchronize()
-                assert code == thd.THD_OK, tag
-                got = out_buf.cpu().numpy()
-                want = O.swap_rows(x_host, w.cu_padded, cp, total, direction).reshape(-1)
-                assert np.array_equal(got[offset:offset + nbytes], want), f"{tag} {direction}"
-                assert (got[:offset] == 0xA5).all() and (got[offset + nbytes:] == 0xA5).all(), f"{tag} {direction}"
-            thd.thd_swap_tuning()
-            route.close()
-    finally:
-        thd.thd_swap_tuning()
+    for case in range(200):
+        cp = int(rng.choice(CPS[1:]))
+        rb = int(rng.choice(ROW_BYTES)) if rng.random() < 0.6 else int(rng.integers(1, 9001))
+        offset = int(rng.choice(OFFSETS + [3, 6, 12]))
+        tune = (int(rng.choice(TUNE_TILE)), int(rng.integers(0, 2)), int(rng.choice(TUNE_BLOCK)),
+                int(rng.choice(TUNE_ORDER)))
+        docs, max_chunk, n_empty = draw_batch(rng, cp, max(1, (2 << 20) // rb))
+        w = W.random_packed([931, case], cp, docs, max_chunk, n_empty, row_shape=(1,), row_dtype="uint8")
+        total = w.total
+        tag = f"shape case {case}: cp {cp} rb {rb} off {offset} T {total} slots {w.n_slots} tuning {tune}"
+        say(tag)
+        route = thd.Route(max(1, w.n_slots), cp, max(total, 1))
+        route.build(dev_i32(w.cu_padded), cp, total)
+        x_host = np.random.default_rng([932, case]).integers(0, 256, (total, rb), dtype=np.uint8)
+        nbytes = total * rb
+        in_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+        out_buf = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+        in_buf[offset:offset + nbytes] = torch.from_numpy(x_host.reshape(-1)).cuda()
+        thd.thd_route_launch_shape(route.handle, *tune)
+        for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+            out_buf.fill_(0xA5)
+            code = thd.thd_swap(route.handle, d, in_buf.data_ptr() + offset, out_buf.data_ptr() + offset, total,
+                                rb)
+            torch.cuda.synchronize()
+            assert code == thd.THD_OK, tag
+            got = out_buf.cpu().numpy()
+            want = O.swap_rows(x_host, w.cu_padded, cp, total, direction).reshape(-1)
+            assert np.array_equal(got[offset:offset + nbytes], want), f"{tag} {direction}"
+            assert (got[:offset] == 0xA5).all() and (got[offset + nbytes:] == 0xA5).all(), f"{tag} {direction}"
+        route.close()
 
 
 def test_fuzz_swap_batch(thd):

@@ -113,36 +113,57 @@ def test_random_swap_parity(thd, case):
         assert (got[:offset] == 0xCD).all() and (got[offset + nbytes:] == 0xCD).all()
 
 
-@pytest.mark.parametrize("tile_bytes,max_wg,nt,block,order,rb", [
-    (1, 0, 1, 256, 1, 48), (1, 7, 0, 512, 2, 48), (1 << 20, 3, 1, 1024, 1, 48), (4096, 1, 0, 128, 2, 48),
-    (20000, 0, 1, 512, 1, 4096), (20000, 5, 0, 1024, 2, 4096), (1000, 0, 1, 128, 2, 4096),
-    (3 * 4096, 13, 1, 256, 1, 4096), (0, 0, 1, 0, 0, 8192), (0, 9, 1, 0, 0, 8192), (0, 0, 0, 0, 0, 8208),
-    (0, 0, 1, 0, 0, 4096), (0, 6, 1, 0, 0, 4096), (0, 0, 1, 0, 2, 2048), (5000, 0, 1, 0, 2, 36),
-    (0, 7, 1, 0, 0, 8), (0, 3, 1, 0, 0, 1), (0, 0, 0, 0, 0, 16), (0, 5, 1, 0, 0, 2),
-    (4096, 0, 1, 128, 64, 4096), (8192, 0, 1, 512, 3, 8192), (0, 11, 1, 0, 1 << 30, 8192), (0, 0, 1, 0, 7, 48),
+@pytest.mark.parametrize("tile_bytes,nt,block,order,rb", [
+    (1, 1, 256, 1, 48), (1, 0, 512, 2, 48), (1 << 20, 1, 1024, 1, 48), (4096, 0, 128, 2, 48),
+    (20000, 1, 512, 1, 4096), (20000, 0, 1024, 2, 4096), (1000, 1, 128, 2, 4096),
+    (3 * 4096, 1, 256, 1, 4096), (0, 1, 0, 0, 8192), (0, 0, 0, 0, 8208),
+    (0, 1, 0, 0, 4096), (0, 1, 0, 2, 2048), (5000, 1, 0, 2, 36),
+    (0, 1, 0, 0, 8), (0, 1, 0, 0, 1), (0, 0, 0, 0, 16), (0, 1, 0, 0, 2),
+    (4096, 1, 128, 64, 4096), (8192, 1, 512, 3, 8192), (0, 1, 0, 1 << 30, 8192), (0, 1, 0, 7, 48),
     # rows cut into slices (tile_bytes below the row size)
-    (4096, 0, 1, 128, 1, 8192), (2048, 0, 1, 128, 64, 8192), (3000, 9, 0, 256, 1, 8208), (16, 0, 1, 128, 5, 4096),
+    (4096, 1, 128, 1, 8192), (2048, 1, 128, 64, 8192), (3000, 0, 256, 1, 8208), (16, 1, 128, 5, 4096),
     # the built-in shape on row sizes between and beyond the measured ones
-    (0, 0, 1, 0, 0, 6144), (0, 0, 1, 0, 0, 4112), (0, 0, 1, 0, 0, 12288), (0, 0, 1, 0, 0, 65536),
-    (0, 0, 1, 0, 0, 10000),
+    (0, 1, 0, 0, 6144), (0, 1, 0, 0, 4112), (0, 1, 0, 0, 12288), (0, 1, 0, 0, 65536),
+    (0, 1, 0, 0, 10000),
 ])
-def test_launch_shapes_do_not_change_results(thd, tile_bytes, max_wg, nt, block, order, rb):
+def test_launch_shapes_do_not_change_results(thd, tile_bytes, nt, block, order, rb):
     import torch
     w = W.random_packed(42, 4, 30, 60, 3, row_shape=(rb,), row_dtype="uint8")
     cu, total = w.cu_padded, w.total
-    say("launch shape", tile_bytes, max_wg, nt, block, order, rb, "T", total)
+    say("launch shape", tile_bytes, nt, block, order, rb, "T", total)
     route = build(thd, cu, 4, total)
     x = torch.from_numpy(w.rows_host()).cuda()
-    try:
-        thd.thd_swap_tuning(tile_bytes, max_wg, nt, block, order)
-        out = route.swap(x, thd.Z2C)
-        back = route.swap(out, thd.C2Z)
-        torch.cuda.synchronize()
-    finally:
-        thd.thd_swap_tuning()
+    thd.thd_route_launch_shape(route.handle, tile_bytes, nt, block, order)
+    out = route.swap(x, thd.Z2C)
+    back = route.swap(out, thd.C2Z)
+    torch.cuda.synchronize()
     want = O.swap_rows(w.rows_host(), cu, 4, total, "z2c")
     assert np.array_equal(out.cpu().numpy(), want)
     assert torch.equal(back, x)
+
+
+def test_launch_shape_belongs_to_its_route(thd):
+    # an override on one route leaves another route of the same batch on the
+    # built-in shape; its field checks run on the host
+    import torch
+    w = W.random_packed(43, 4, 20, 40, 2, row_shape=(4096,), row_dtype="uint8")
+    cu, total = w.cu_padded, w.total
+    say("launch shape per route, T", total)
+    a = build(thd, cu, 4, total)
+    b = build(thd, cu, 4, total)
+    for bad in ((-1, 1, 0, 0), (0, 2, 0, 0), (0, -1, 0, 0), (0, 1, 300, 0), (0, 1, 0, -1)):
+        with pytest.raises(thd.ThdError):
+            thd.thd_route_launch_shape(a.handle, *bad)
+    thd.thd_route_launch_shape(a.handle, 1000, 0, 512, 3)
+    x = torch.from_numpy(w.rows_host()).cuda()
+    out_a = a.swap(x, thd.Z2C)
+    out_b = b.swap(x, thd.Z2C)
+    torch.cuda.synchronize()
+    want = O.swap_rows(w.rows_host(), cu, 4, total, "z2c")
+    assert np.array_equal(out_a.cpu().numpy(), want)
+    assert np.array_equal(out_b.cpu().numpy(), want)
+    thd.thd_route_launch_shape(a.handle)  # back to the built-in shape
+    assert torch.equal(a.swap(x, thd.Z2C), out_b)
 
 
 # ---- label shift / MTP roll / valid mask ----
