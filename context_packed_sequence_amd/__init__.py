@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     THD_CONTIGUOUS_TO_ZIGZAG,
+    THD_PACK_STATIC_BYTES,
     THD_ERR_ALIAS,
     THD_ERR_ARG,
     THD_ERR_CAPACITY,
@@ -44,6 +45,7 @@ from .binding import (  # noqa: F401
     thd_read_stream,
     thd_write_stream,
     thd_pack,
+    thd_pack_noalloc,
     thd_pack_workspace_bytes,
     thd_roll_labels,
     thd_roll_labels_zigzag,

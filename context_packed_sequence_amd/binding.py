@@ -46,12 +46,13 @@ THD_MAX_CP = 1024
 THD_MAX_SHIFT = 8
 THD_MAX_BATCH = 16
 THD_PACK_MAX_SEQ = 2147479552
+THD_PACK_STATIC_BYTES = 1048576
 
 EXPORTS = (
     "thd_route_create", "thd_route_destroy", "thd_build_route", "thd_swap", "thd_roll_labels",
     "thd_route_status", "thd_route_copy_out", "thd_route_info", "thd_strerror",
     "thd_swap_batch", "thd_roll_labels_zigzag", "thd_pack_workspace_bytes", "thd_pack", "thd_copy",
-    "thd_route_launch_shape", "thd_read_stream", "thd_write_stream",
+    "thd_route_launch_shape", "thd_read_stream", "thd_write_stream", "thd_pack_noalloc",
 )
 
 
@@ -90,6 +91,8 @@ def _load() -> ctypes.CDLL:
         "thd_write_stream": (ctypes.c_int, [c_p, c_i64, ctypes.c_uint32, c_p]),
         "thd_pack": (ctypes.c_int, [c_p, c_i32, c_i32, c_i64, c_i64, c_i32, c_i64, c_i32, c_i64, c_p, c_i64, c_p,
                                     c_p, c_p, c_p, c_p]),
+        "thd_pack_noalloc": (ctypes.c_int, [c_p, c_i32, c_i32, c_i64, c_i64, c_i32, c_i64, c_i32, c_i64, c_p, c_p,
+                                            c_p, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -193,6 +196,14 @@ def thd_pack(tokens, batch: int, seq: int, pad_id: int, eod_id: int, align: int,
     return _check(_lib.thd_pack(_ptr(tokens), batch, seq, pad_id, eod_id, align, capacity, max_docs, pad_value,
                                 _ptr(workspace), workspace_bytes, _ptr(packed), _ptr(cu_seqlens),
                                 _ptr(cu_seqlens_padded), _ptr(status), _stream(stream)), "thd_pack")
+
+
+def thd_pack_noalloc(tokens, batch: int, seq: int, pad_id: int, eod_id: int, align: int, capacity: int,
+                     max_docs: int, pad_value: int, packed, cu_seqlens, cu_seqlens_padded, status,
+                     stream=None) -> int:
+    return _check(_lib.thd_pack_noalloc(_ptr(tokens), batch, seq, pad_id, eod_id, align, capacity, max_docs,
+                                        pad_value, _ptr(packed), _ptr(cu_seqlens), _ptr(cu_seqlens_padded),
+                                        _ptr(status), _stream(stream)), "thd_pack_noalloc")
 
 
 def thd_copy(x, out, nbytes: int, stream=None) -> int:

@@ -5,6 +5,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -320,6 +321,34 @@ PackLayout pack_layout(int32_t batch, int32_t seq) {
 
 }  // namespace
 
+// Device scratch of thd_pack_noalloc, in place of the caller's workspace: a
+// file-scope array, one copy on every GPU the library runs on, held until
+// the process ends.  In host code its name is only a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[THD_PACK_STATIC_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of `scratch` on `device` (the current device), looked up on the
+// first call for that device and kept.
+int scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return THD_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return THD_ERR_HIP;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return THD_OK;
+}
+
+}  // namespace
+
 int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq) {
   if (batch < 0 || seq < 0 || seq > THD_PACK_MAX_SEQ) return -1;
   return pack_layout(batch, seq).bytes;
@@ -363,6 +392,22 @@ int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, 
                          pad_value, ws, packed, cu_seqlens, cu_seqlens_padded, status, as_stream(stream)) != hipSuccess)
     return THD_ERR_HIP;
   return THD_OK;
+}
+
+int thd_pack_noalloc(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id, int32_t align,
+                     int64_t capacity, int32_t max_docs, int64_t pad_value, int64_t* packed, int32_t* cu_seqlens,
+                     int32_t* cu_seqlens_padded, int32_t* status, void* stream) {
+  if (batch < 0 || seq < 0 || seq > THD_PACK_MAX_SEQ) return THD_ERR_ARG;
+  if (pack_layout(batch, seq).bytes > THD_PACK_STATIC_BYTES) return THD_ERR_CAPACITY;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return THD_ERR_HIP;
+  void* ws = nullptr;
+  const int rc = scratch_address(device, &ws);
+  if (rc != THD_OK) return rc;
+  // nothing in the scratch has to start at zero: every word a pack reads was
+  // written earlier in the same call
+  return thd_pack(tokens, batch, seq, pad_id, eod_id, align, capacity, max_docs, pad_value, ws,
+                  THD_PACK_STATIC_BYTES, packed, cu_seqlens, cu_seqlens_padded, status, stream);
 }
 
 int thd_route_status(const thd_route* route, void* stream, int32_t* host_status) {

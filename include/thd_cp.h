@@ -75,6 +75,7 @@ extern "C" {
 #define THD_MAX_SHIFT     8
 #define THD_MAX_BATCH     16
 #define THD_PACK_MAX_SEQ  2147479552   /* 2^31 - 4096 tokens per packed row */
+#define THD_PACK_STATIC_BYTES 1048576   /* device scratch of thd_pack_noalloc (1 MiB per GPU) */
 
 typedef struct thd_route thd_route;   /* opaque; owns one device workspace */
 
@@ -259,6 +260,32 @@ int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq);
 int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id, int32_t align,
              int64_t capacity, int32_t max_docs, int64_t pad_value, void* workspace, int64_t workspace_bytes,
              int64_t* packed, int32_t* cu_seqlens, int32_t* cu_seqlens_padded, int32_t* status, void* stream);
+
+/*
+ * thd_pack_noalloc -- thd_pack for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, outputs and
+ * errors as thd_pack, minus the workspace: the pack runs in a device scratch
+ * array of THD_PACK_STATIC_BYTES inside the library, one per GPU, held until
+ * the process ends.  It allocates nothing and frees nothing.
+ *
+ * Size limit: batches whose thd_pack_workspace_bytes(batch, seq) exceeds
+ * THD_PACK_STATIC_BYTES (about 23,700 chunks of 1024 tokens, i.e. about 24
+ * million tokens in [batch, seq]) return THD_ERR_CAPACITY before any device
+ * work.  The first call on a device looks up that device's scratch address
+ * (hipGetSymbolAddress, host only); make one call before capturing a graph
+ * if the capture mode forbids runtime calls.  THD_ERR_HIP if the lookup
+ * fails.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls whose work
+ * overlaps on one GPU (on different streams, or from different threads,
+ * with no ordering between them) race and may produce wrong outputs.
+ * Calls ordered on one stream are safe.  Nothing in the scratch has to
+ * start at zero.  Stream-ordered, three kernel launches, like thd_pack.
+ */
+int thd_pack_noalloc(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id,
+                     int32_t align, int64_t capacity, int32_t max_docs, int64_t pad_value, int64_t* packed,
+                     int32_t* cu_seqlens, int32_t* cu_seqlens_padded, int32_t* status, void* stream);
 
 /*
  * thd_route_status -- SYNC.  Waits for `stream`, then stores the status word

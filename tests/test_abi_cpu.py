@@ -126,6 +126,17 @@ def test_host_rejections_without_device_work(pkg):
     assert lib.thd_write_stream(None, 0, 0, None) == pkg.THD_OK
     # the launch-shape override belongs to a route: none given, nothing set
     assert lib.thd_route_launch_shape(None, 0, 1, 0, 0) == pkg.THD_ERR_ARG
+    # the pack without allocation: bad sizes, and batches beyond its static
+    # scratch, are refused on the host before the scratch is looked up
+    def pack_noalloc(batch, seq):
+        return lib.thd_pack_noalloc(None, batch, seq, 0, 1, 8, 8, 1, 0, None, None, None, None, None)
+    assert pack_noalloc(-1, 8) == pkg.THD_ERR_ARG
+    assert pack_noalloc(1, pkg.THD_PACK_MAX_SEQ + 1) == pkg.THD_ERR_ARG
+    seq = 1024
+    while lib.thd_pack_workspace_bytes(2, seq + 1024) <= pkg.THD_PACK_STATIC_BYTES:
+        seq += 1024
+    assert seq * 2 > 20_000_000                      # the limit admits about 24 million tokens
+    assert pack_noalloc(2, seq + 1024) == pkg.THD_ERR_CAPACITY
 
 
 def test_package_and_oracle_share_no_code():
