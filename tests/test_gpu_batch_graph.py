@@ -251,6 +251,90 @@ def test_graph_capture_replays_build_swaps_and_roll(thd):
         assert np.array_equal(shifted[k].cpu().numpy(), want_s[k])
 
 
+def test_graph_capture_of_the_full_microbatch(thd):
+    # The configured 48-layer micro-batch (cp 16, T = 262144, rows of 4 KiB):
+    # route build, 48 x (z->c, c->z) and the zigzag label roll with MTP
+    # depths 1..3 (shifts 1..4) captured in one HIP graph.  Replays with eager
+    # work in between, then one replay after a second batch (same token and
+    # slot counts, documents reordered, other rows and ids) is written into the
+    # captured inputs; every replay is checked against the oracle.
+    import torch
+    wa = W.make("full")
+    total, cp, n_slots, J = wa.total, wa.cp, wa.n_slots, wa.max_shift
+    perm = np.random.default_rng(11).permutation(n_slots)
+    wb = W.Workload("full-reordered", 101, cp, W.cumulative(np.diff(wa.cu_padded)[perm]),
+                    W.cumulative(np.diff(wa.cu_real)[perm]), wa.row_shape, max_shift=J, layers=wa.layers,
+                    seed_extra=(502,))
+    assert not np.array_equal(wb.cu_padded, wa.cu_padded) and wb.total == total
+    say("full micro-batch graph: T", total, "cp", cp, "layers", wa.layers)
+    route = thd.Route(n_slots, cp, total)
+    cu, cu_real = dev_i32(wa.cu_padded), dev_i32(wa.cu_real)
+    ids = dev_i64(wa.ids())
+
+    def rows_for(seed):
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        v = torch.randn((total,) + tuple(wa.row_shape), dtype=torch.bfloat16, device="cuda", generator=g)
+        v.view(total, -1).view(torch.int64)[:, 0] = torch.arange(total, device="cuda")   # row stamps
+        return v
+
+    x = rows_for(W.BASE_SEED + wa.index)
+    a, b = torch.empty_like(x), torch.empty_like(x)
+    rb = wa.row_bytes
+    shifted = torch.empty((J, total), dtype=torch.int64, device="cuda")
+    mask = torch.empty((J + 1, total), dtype=torch.uint8, device="cuda")
+    status = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def step(stream):
+        thd.thd_build_route(route.handle, cu, n_slots, cp, total, stream)
+        for _ in range(wa.layers):
+            thd.thd_swap(route.handle, thd.Z2C, x, a, total, rb, stream)
+            thd.thd_swap(route.handle, thd.C2Z, a, b, total, rb, stream)
+        thd.thd_roll_labels_zigzag(route.handle, ids, cu, cu_real, n_slots, total, J, 0, shifted, mask, status,
+                                   stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s.cuda_stream)                          # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+    def check(w):
+        assert route.status() == 0 and int(status.item()) == 0
+        xh = x.view(total, -1).view(torch.int16).cpu().numpy()
+        want_a = O.swap_rows(xh, w.cu_padded, cp, total, "z2c")
+        assert np.array_equal(a.view(total, -1).view(torch.int16).cpu().numpy(), want_a)
+        assert torch.equal(b.view(torch.int16), x.view(torch.int16))
+        ws_, wm_ = O.roll_labels(w.ids(), w.cu_padded, w.cu_real, total, J, 0)
+        for k in range(J):
+            assert np.array_equal(shifted[k].cpu().numpy(), O.swap_rows(ws_[k], w.cu_padded, cp, total, "c2z"))
+        for k in range(J + 1):
+            assert np.array_equal(mask[k].cpu().numpy(), O.swap_rows(wm_[k], w.cu_padded, cp, total, "c2z"))
+
+    for rep in range(2):
+        a.zero_(); b.zero_(); shifted.fill_(-1); mask.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("full micro-batch graph replay", rep)
+        check(wa)
+        _ = (x.view(torch.int16)[:1024].float().sum() + 1).item()   # eager work between replays
+    cu.copy_(dev_i32(wb.cu_padded))
+    cu_real.copy_(dev_i32(wb.cu_real))
+    x.copy_(rows_for(W.BASE_SEED + 77))
+    ids.copy_(dev_i64(wb.ids()))
+    a.zero_(); b.zero_(); shifted.fill_(-1); mask.fill_(7)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    say("full micro-batch graph replay with new boundaries")
+    check(wb)
+
+
 def test_graph_capture_of_the_whole_chain_from_token_rows(thd):
     # Pack -> route build -> zigzag roll -> multi-key swap captured in one
     # HIP graph (every shape fixed on the host by the token budget); replays
