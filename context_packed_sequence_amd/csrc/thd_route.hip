@@ -102,7 +102,12 @@ constexpr int kBuildLdsBytes = 150 * 1024;  // of the 160 KiB a workgroup may ho
 // LDS copy.  One launch instead of build + directory, and no workgroup ever
 // waits for another.
 constexpr int kFusedMaxSegments = 16384;
-constexpr int kDirPerFusedGroup = 1024;  // directory rows per workgroup and direction
+constexpr int kDirPerFusedGroup = 1024;  // directory rows per workgroup and direction, below the cap
+// Cap on the fused build's workgroups.  Each one builds the whole route in its
+// own LDS, so past a couple per CU more of them only repeat that build: a
+// batch of 2^31 tokens would otherwise launch 131072 of them.  Above the cap
+// every workgroup writes an equal, larger share of the directory.
+constexpr int kFusedMaxGroups = 512;
 
 // Largest i in [lo, hi) with runs[i].out <= row, given runs[lo].out <= row.
 __device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, int32_t lo, int32_t hi, int32_t row) {
@@ -132,7 +137,7 @@ template <bool kLds, bool kFused>
 __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
                                                                     int32_t cp, int32_t total, RouteDev ws,
                                                                     int32_t lds_run_cap, FastDiv div_share,
-                                                                    FastDiv div_two_cp) {
+                                                                    FastDiv div_two_cp, int32_t dir_per_group) {
   // kLds: docs[3 * n_slots], split[copies * cp * cp]; kFused adds, 8-byte
   // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
   extern __shared__ int32_t s_dyn[];
@@ -335,8 +340,9 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     // ---- 6. this workgroup's share of the directory, both directions ----
     if (s_sev) return;  // a failed route is never read past its status
     const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
-    const int32_t b0 = blockIdx.x * kDirPerFusedGroup;
-    const int32_t b1 = min(n_blocks, b0 + kDirPerFusedGroup);
+    const int32_t b0 = static_cast<int32_t>(min(static_cast<int64_t>(blockIdx.x) * dir_per_group,
+                                                static_cast<int64_t>(n_blocks)));
+    const int32_t b1 = static_cast<int32_t>(min(static_cast<int64_t>(n_blocks), static_cast<int64_t>(b0) + dir_per_group));
     for (int32_t b = b0 + tid; b < b1; b += kBuildThreads) {
       const int32_t row = b << kDirShift;
       ws.dir_dst[b] = dir_entry(l_dst, last_run_at_or_before(l_dst, 0, n_dst, row), n_dst, row, total);
@@ -443,16 +449,18 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
     const int32_t run_cap = 2 * cp * n_slots + cp;
     const int64_t lds_fused = build_lds_bytes(n_slots, cp, true);
     const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
-    const int32_t grid = n_blocks > 0 ? (n_blocks + kDirPerFusedGroup - 1) / kDirPerFusedGroup : 1;
+    int32_t grid = n_blocks > 0 ? (n_blocks + kDirPerFusedGroup - 1) / kDirPerFusedGroup : 1;
+    if (grid > kFusedMaxGroups) grid = kFusedMaxGroups;
+    const int32_t dir_per_group = n_blocks > 0 ? (n_blocks + grid - 1) / grid : kDirPerFusedGroup;
     hipLaunchKernelGGL((route_build_kernel<true, true>), dim3(grid), dim3(kBuildThreads),
                        static_cast<size_t>(lds_fused), stream, cu, n_slots, cp, total, ws, run_cap, div_share,
-                       div_two_cp);
+                       div_two_cp, dir_per_group);
   } else if (lds <= kBuildLdsBytes) {
     hipLaunchKernelGGL((route_build_kernel<true, false>), dim3(1), dim3(kBuildThreads), static_cast<size_t>(lds),
-                       stream, cu, n_slots, cp, total, ws, 0, div_share, div_two_cp);
+                       stream, cu, n_slots, cp, total, ws, 0, div_share, div_two_cp, 0);
   } else {
     hipLaunchKernelGGL((route_build_kernel<false, false>), dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp,
-                       total, ws, 0, div_share, div_two_cp);
+                       total, ws, 0, div_share, div_two_cp, 0);
   }
   return hipGetLastError();
 }

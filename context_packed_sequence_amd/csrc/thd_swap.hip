@@ -446,6 +446,10 @@ int64_t whole_row_tile(int64_t row_bytes, int64_t tile_bytes) {
   return tile_bytes / row_bytes / q * q;
 }
 
+// A dispatch counts its work-items in 32 bits: a launch past that is refused
+// on the host rather than handed to the runtime.
+bool fits_dispatch(int64_t workgroups, int64_t threads) { return workgroups * threads <= static_cast<int64_t>(UINT32_MAX); }
+
 int copy_unit(int64_t row_bytes, const void* in, const void* out) {
   const uint64_t align_bits = static_cast<uint64_t>(row_bytes) | reinterpret_cast<uintptr_t>(in) |
                               reinterpret_cast<uintptr_t>(out);
@@ -495,6 +499,7 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
     constexpr int kBlock = 256;
     const int64_t tiles = (static_cast<int64_t>(total) + kBlock * kSmallRowsPerThread - 1) /
                           (kBlock * kSmallRowsPerThread);
+    if (!fits_dispatch(tiles, kBlock)) return hipErrorInvalidValue;
     const int32_t grid = static_cast<int32_t>(tiles);
     if (grid <= 0) return hipSuccess;
     const auto* i8 = static_cast<const unsigned char*>(in);
@@ -572,6 +577,7 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   if (slots > INT32_MAX) return hipErrorInvalidValue;
   sh.grid = static_cast<int32_t>(slots);
   if (sh.grid <= 0) return hipSuccess;
+  if (!fits_dispatch(sh.grid, unit == 16 ? block : 256)) return hipErrorInvalidValue;
   const bool nt = cfg.nontemporal != 0;
 #define THD_SWAP_ARGS hdr, runs, runs_word, dir, in, out, total, row_bytes, sh, nt, stream
   switch (unit) {
@@ -639,6 +645,7 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
   const int64_t slots = args.chunk == 1 ? tiles : (tiles + kXcds * args.chunk - 1) / (kXcds * args.chunk) * kXcds * args.chunk;
   if (slots > INT32_MAX) return hipErrorInvalidValue;
   args.n_slots = static_cast<int32_t>(slots);
+  if (!fits_dispatch(slots, kBatchBlock)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(swap_batch_kernel, dim3(static_cast<unsigned>(slots)), dim3(kBatchBlock), 0, stream, hdr,
                      runs_word, runs, dir, total, args);
   return hipGetLastError();
@@ -656,7 +663,7 @@ hipError_t launch_copy(const void* in, void* out, int64_t bytes, hipStream_t str
   if (chunk > per_xcd) chunk = per_xcd;
   const int64_t slots =
       chunk == 1 ? n_tiles : (static_cast<int64_t>(n_tiles) + kXcds * chunk - 1) / (kXcds * chunk) * kXcds * chunk;
-  if (slots > INT32_MAX) return hipErrorInvalidValue;
+  if (slots > INT32_MAX || !fits_dispatch(slots, unit == 16 ? 128 : 256)) return hipErrorInvalidValue;
   const auto* i8 = static_cast<const unsigned char*>(in);
   auto* o8 = static_cast<unsigned char*>(out);
   const dim3 grid(static_cast<unsigned>(slots));

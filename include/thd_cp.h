@@ -111,8 +111,9 @@ void thd_route_destroy(thd_route* route);
  * output row of each direction, the input row feeding it, the end of its run,
  * the run's index and which of the 16 rows start a run.  When 2*cp*n_slots
  * <= 16384 and the route fits in 150 KiB of LDS this is one launch of
- * ceil(total_tokens / 16384) workgroups, each building the route in its own
- * LDS and writing its share of the directory; larger batches take one
+ * ceil(total_tokens / 16384) workgroups, at most 512, each building the route
+ * in its own LDS and writing an equal share of the directory; larger batches
+ * take one
  * single-workgroup build launch (in LDS, or in the route's workspace when
  * LDS is too small) and one grid-wide directory launch.  Results and the
  * status word stay on the device.

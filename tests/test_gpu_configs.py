@@ -192,6 +192,97 @@ def test_maximum_size_swap(thd):
     torch.cuda.empty_cache()
 
 
+def _many_documents(total, n, align, seed):
+    rng = np.random.default_rng([W.BASE_SEED, seed])
+    raw = rng.integers(1, 1000, n).astype(np.float64)
+    lens = (np.floor(raw / raw.sum() * total / align) * align).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    assert (lens % align == 0).all() and lens.sum() == total and (lens > 0).all()
+    return W.cumulative(lens)
+
+
+def test_route_build_above_the_workgroup_cap(thd):
+    # T = 2**24 over 520 documents at cp 8 (8320 zigzag segments, the
+    # one-launch build): 2**20 directory blocks, more than the capped grid
+    # covers at 1024 per workgroup, so each workgroup writes a larger share.
+    # 16-byte rows with 16-byte tiles make every row its own tile, so every
+    # directory entry is read by the swap; every output row is then compared
+    # with the input row the oracle's zigzag layout names for it (c->z: row i
+    # holds token zigzag[i]; z->c: token g comes from the row holding it).
+    import torch
+    cp, total = 8, 1 << 24
+    cu = _many_documents(total, 520, 2 * cp, 78)
+    say("route above the workgroup cap: T", total, "slots", len(cu) - 1)
+    route = thd.Route(len(cu) - 1, cp, total)
+    route.build(dev_i32(cu), cp, total)
+    assert route.status() == 0
+    zig = O.layout_tokens(cu, cp, total, O.ZIGZAG)
+    row_of = np.empty_like(zig)
+    row_of[zig] = np.arange(total, dtype=zig.dtype)
+    g = torch.Generator(device="cuda").manual_seed(W.BASE_SEED + 79)
+    x = torch.empty((total, 16), dtype=torch.uint8, device="cuda")
+    x.view(torch.int64).random_(generator=g)
+    thd.thd_route_launch_shape(route.handle, 16, 1, 0, 0)
+    for direction, d, src in (("z2c", thd.Z2C, row_of), ("c2z", thd.C2Z, zig)):
+        out = route.swap(x, d)
+        torch.cuda.synchronize()
+        assert_every_row_from_oracle_source(out, x, src)
+        del out
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_maximum_size_route_with_many_documents(thd):
+    # T = 2**31 - 64 tokens over 520 documents at cp 8: the build (one
+    # launch, its grid capped) stays within a few milliseconds, every run
+    # starts and ends where the oracle's single-token form puts its tokens,
+    # and a 1-byte-row swap matches that form on sampled tokens and returns
+    # the input on the round trip.
+    import torch
+    cp, total = 8, 2 ** 31 - 64
+    cu = _many_documents(total, 520, 2 * cp, 80)
+    say("maximum size, many documents: T", total, "slots", len(cu) - 1)
+    route = thd.Route(len(cu) - 1, cp, total)
+    cu_d = dev_i32(cu)
+    route.build(cu_d, cp, total)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        route.build(cu_d, cp, total)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    say("build ms", [round(t, 3) for t in times])
+    assert float(np.median(times)) < 5.0
+    assert route.status() == 0
+    by_src, by_dst, split = route.copy_out()
+    share = total // cp
+    assert (split.astype(np.int64).sum(0) == share).all() and (split.astype(np.int64).sum(1) == share).all()
+    for order, col in ((by_src, 0), (by_dst, 1)):
+        starts = order[:, col].astype(np.int64)
+        assert starts[0] == 0 and np.array_equal(starts[1:], starts[:-1] + order[:-1, 2])
+    for zrow, tok, n in by_src.astype(np.int64):
+        for off in (0, n - 1):
+            assert O.zigzag_position(cu, cp, total, int(tok + off)) == zrow + off
+    x = torch.randint(0, 256, (total, 1), dtype=torch.uint8, device="cuda")
+    out = route.swap(x, thd.Z2C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    toks = np.unique(np.concatenate([rng.integers(0, total, 3000), by_src[:, 1].astype(np.int64),
+                                     by_src[:, 1].astype(np.int64) + by_src[:, 2] - 1, [0, total - 1]]))
+    src = np.array([O.zigzag_position(cu, cp, total, int(t)) for t in toks], dtype=np.int64)
+    got = out.view(-1).index_select(0, torch.from_numpy(toks).cuda()).cpu().numpy()
+    want = x.view(-1).index_select(0, torch.from_numpy(src).cuda()).cpu().numpy()
+    assert np.array_equal(got, want)
+    back = route.swap(out, thd.C2Z)
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    del x, out, back, route
+    torch.cuda.empty_cache()
+
+
 def test_maximum_size_swap_wide_rows(thd):
     # T = 2**31 - 64 tokens of 16-byte rows (the widest copy unit): 32 GiB
     # per buffer, so every byte offset past 2**31 and 2**32 is exercised on
