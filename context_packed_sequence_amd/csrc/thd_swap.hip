@@ -365,52 +365,54 @@ struct BatchArgs {
   int32_t n;
   int32_t total_tiles;
   int32_t chunk;    // tiles per XCD chunk (1: natural order), as in swap_kernel
-  int32_t n_slots;  // workgroup slots: total_tiles rounded up to whole chunk rounds
 };
 
 constexpr int kBatchBlock = 128;
 
+// One tile per workgroup; the tile's tensor is found in the kernel arguments,
+// then the route status, run count and directory entry of the tile's first
+// row are read in one round trip, as in swap_kernel.
 __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))) void swap_batch_kernel(const int32_t* __restrict__ hdr, int runs_word,
                                                                  const RunPair* __restrict__ runs,
                                                                  const DirEntry* __restrict__ dir, int32_t total,
                                                                  BatchArgs args) {
   __shared__ RunPair s_runs[kSmallStage];
   __shared__ int32_t s_k[2];
-  if (hdr[kHdrStatus] != THD_OK) return;
+  const int32_t g = tile_of_slot(blockIdx.x, args.chunk);
+  if (g >= args.total_tiles) return;
+  int i = 0;
+  while (i + 1 < args.n && args.t[i + 1].first_tile <= g) ++i;
+  const BatchTensor bt = args.t[i];
+  // first output row of the tile (long rows: tile = (row, slice))
+  const int32_t r = bt.parts > 1 ? (g - bt.first_tile) / bt.parts
+                                 : static_cast<int32_t>(static_cast<int64_t>(g - bt.first_tile) * bt.tile_rows);
+  const int32_t status = hdr[kHdrStatus];
   const int32_t n_runs = hdr[runs_word];
-  for (int32_t slot = blockIdx.x; slot < args.n_slots; slot += gridDim.x) {
-    const int32_t g = tile_of_slot(slot, args.chunk);
-    if (g >= args.total_tiles) continue;
-    int i = 0;
-    while (i + 1 < args.n && args.t[i + 1].first_tile <= g) ++i;
-    const BatchTensor bt = args.t[i];
-    if (bt.parts > 1) {  // long rows (16-byte units only): one slice of one row per tile
-      const int32_t r = (g - bt.first_tile) / bt.parts;
-      const int64_t b0 = static_cast<int64_t>((g - bt.first_tile) % bt.parts) * bt.part_bytes;
-      const int64_t b1 = min(bt.row_bytes, b0 + bt.part_bytes);
-      swap_row_part<u32x4, kBatchBlock, 8, true>(runs, dir[r >> kDirShift], n_runs, bt.in, bt.out, bt.row_bytes, r,
-                                                 b0, b1);
-      continue;
-    }
-    const int32_t r0 = static_cast<int32_t>(static_cast<int64_t>(g - bt.first_tile) * bt.tile_rows);
-    const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r0) + bt.tile_rows));
-    if (bt.small) {  // one unit per row, short runs: the LDS-staged small-row path
-      switch (bt.unit) {
-        case 8: swap_tile_small<u32x2, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
-        case 4: swap_tile_small<uint32_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
-        case 2: swap_tile_small<uint16_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
-        default: swap_tile_small<uint8_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r0, r1, s_runs, s_k); break;
-      }
-      continue;
-    }
-    const DirEntry& e = dir[r0 >> kDirShift];
+  const DirEntry e = dir[r >> kDirShift];
+  asm volatile("" ::"s"(status), "s"(n_runs), "s"(e.in), "s"(e.run_end), "s"(e.run), "s"(e.starts));
+  if (status != THD_OK) return;  // a failed build writes nothing
+  if (bt.parts > 1) {  // long rows (16-byte units only): one slice of one row per tile
+    const int64_t b0 = static_cast<int64_t>((g - bt.first_tile) % bt.parts) * bt.part_bytes;
+    const int64_t b1 = min(bt.row_bytes, b0 + bt.part_bytes);
+    swap_row_part<u32x4, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, bt.row_bytes, r, b0, b1);
+    return;
+  }
+  const int32_t r1 = static_cast<int32_t>(min(static_cast<int64_t>(total), static_cast<int64_t>(r) + bt.tile_rows));
+  if (bt.small) {  // one unit per row, short runs: the LDS-staged small-row path
     switch (bt.unit) {
-      case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 8: swap_tile<u32x2, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 4: swap_tile<uint32_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      case 2: swap_tile<uint16_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
-      default: swap_tile<uint8_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r0, r1); break;
+      case 8: swap_tile_small<u32x2, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r, r1, s_runs, s_k); break;
+      case 4: swap_tile_small<uint32_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r, r1, s_runs, s_k); break;
+      case 2: swap_tile_small<uint16_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r, r1, s_runs, s_k); break;
+      default: swap_tile_small<uint8_t, kBatchBlock, true>(runs, dir, n_runs, bt.in, bt.out, total, r, r1, s_runs, s_k); break;
     }
+    return;
+  }
+  switch (bt.unit) {
+    case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    case 8: swap_tile<u32x2, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    case 4: swap_tile<uint32_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    case 2: swap_tile<uint16_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    default: swap_tile<uint8_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
   }
 }
 
@@ -644,7 +646,6 @@ hipError_t launch_swap_batch(const int32_t* hdr, const RunPair* runs, int runs_w
   args.chunk = static_cast<int32_t>(per_xcd < 64 ? per_xcd : 64);
   const int64_t slots = args.chunk == 1 ? tiles : (tiles + kXcds * args.chunk - 1) / (kXcds * args.chunk) * kXcds * args.chunk;
   if (slots > INT32_MAX) return hipErrorInvalidValue;
-  args.n_slots = static_cast<int32_t>(slots);
   if (!fits_dispatch(slots, kBatchBlock)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(swap_batch_kernel, dim3(static_cast<unsigned>(slots)), dim3(kBatchBlock), 0, stream, hdr,
                      runs_word, runs, dir, total, args);
