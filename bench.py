@@ -69,7 +69,10 @@ ROW_SWEEP_BYTES = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 64, 100, 128, 256, 512,
 def row_sweep(workloads):
     """Swap bandwidth against row size: the 128K workload's document mix
     scaled so that one swap moves about 1 GiB, every row size through the
-    same route shape; a plain copy of the same bytes alongside."""
+    same route shape; a plain copy of the same bytes alongside.  Each size
+    first runs its swaps back to back for 0.15 s (the clocks rise only under
+    sustained load), then swap pairs and copies are timed in interleaved
+    samples of about 3 ms of back-to-back launches."""
     import numpy as np
     import torch
 
@@ -91,15 +94,25 @@ def row_sweep(workloads):
         a = torch.empty_like(x)
         b = torch.empty_like(x)
         nbytes = total * rb
-        swaps = [lambda: thd.thd_swap(route.handle, thd.Z2C, x, a, total, rb, sh),
-                 lambda: thd.thd_swap(route.handle, thd.C2Z, a, b, total, rb, sh)]
-        for f in swaps * 2:
-            f()
+
+        def pair():
+            thd.thd_swap(route.handle, thd.Z2C, x, a, total, rb, sh)
+            thd.thd_swap(route.handle, thd.C2Z, a, b, total, rb, sh)
+
+        pair()
         torch.cuda.synchronize()
         assert torch.equal(b, x), rb
-        t_swap = _median_event_ms(torch, stream, lambda: [f() for f in swaps], 10) / 2
-        thd.thd_copy(x, a, nbytes, sh)
-        t_copy = _median_event_ms(torch, stream, lambda: thd.thd_copy(x, a, nbytes, sh), 10)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.15:
+            for _ in range(10):
+                pair()
+            torch.cuda.synchronize()
+        t_swap, t_copy = [], []
+        for _ in range(8):
+            t_swap += [t / 20 for t in _event_samples(torch, stream, lambda: [pair() for _ in range(10)], 1)]
+            t_copy += [t / 20 for t in _event_samples(torch, stream, lambda: [thd.thd_copy(x, a, nbytes, sh)
+                                                                           for _ in range(20)], 1)]
+        t_swap, t_copy = float(np.median(t_swap)), float(np.median(t_copy))
         swap_gbps = 2 * nbytes / (t_swap * 1e-3) / 1e9
         copy_gbps = 2 * nbytes / (t_copy * 1e-3) / 1e9
         print(json.dumps({"row_bytes": rb, "tokens": total, "cp_size": cp, "swap_us": round(t_swap * 1e3, 2),
