@@ -521,39 +521,45 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
     return hipGetLastError();
   }
 
-  // Launch shape.  Measured on MI355X (head-to-head sweeps on one box,
-  // repeated on a second): with 16-byte units every workgroup moves about
-  // 4 KiB.  Rows of 4 KiB up to 8 KiB: one row per 256-thread workgroup,
-  // XCD-chunked order with chunks of 256 tiles (0.6-1 % over chunks of 128
-  // since the status, run count and directory reads share one round trip).
-  // Rows of 8 KiB and more:
-  // 4 KiB slices of one row (whole 128-byte lines where the row is made of
-  // them) per 128-thread workgroup, chunks of 64.  Rows of 1-4 KiB: see
-  // below.  Shorter rows: 4 KiB tiles of whole rows, 128 threads, natural
-  // order.  Units under 16 bytes: 256 threads, 8 KiB tiles, chunks of 64.
-  // Every field can be overridden per route for sweeps; a tile size below
-  // the row size cuts rows into slices.
-  const bool big_rows = unit == 16 && row_bytes >= 8192;
-  const bool mid_rows = unit == 16 && row_bytes >= 4096 && !big_rows;
-  // rows between 1 and 4 KiB that are not powers of two: rows of whole
-  // 128-byte lines are grouped into tiles of at least 4 KiB on 256 threads,
-  // as the 4-8 KiB rows; other sizes go one row per 128-thread workgroup
-  // (1 KiB and 2 KiB rows keep the 4 KiB tiles of the shorter rows)
-  const bool kib_rows =
-      unit == 16 && row_bytes > 1024 && row_bytes < 4096 && (row_bytes & (row_bytes - 1)) != 0;
-  const bool kib_lines = kib_rows && row_bytes % 128 == 0;
-  const int64_t tile_bytes =
-      cfg.tile_bytes > 0 ? cfg.tile_bytes
-                         : (mid_rows || (kib_rows && !kib_lines) ? row_bytes : (unit == 16 ? 4096 : unit_tile_bytes));
-  const int block = cfg.block_threads > 0 ? cfg.block_threads
-                                          : (unit == 16 ? (mid_rows || kib_lines ? 256 : 128) : 256);
+  // Launch shape, measured on MI355X (interleaved sweeps on one box, 1 GiB
+  // per swap, after a warm-up).  Rows moved in 16-byte units run fastest when
+  // every 256-thread workgroup moves 4-6 KiB, one or at most one and a half
+  // 16-byte words per lane:
+  //  * rows of whole 4 KiB pages (4, 8, 12, 16 KiB, ...): one 4 KiB slice of
+  //    a row per workgroup, one word per lane, XCD-chunked order with chunks
+  //    of 256 tiles (8-16 KiB rows 1.2-1.5 % faster than 4 KiB slices on 128
+  //    threads with two words per lane);
+  //  * other rows above 4 KiB (5120, 6144, 10240, ...): slices of 4-6 KiB,
+  //    chunks of 64 (5120- and 6144-byte rows 2-3 % faster than one row per
+  //    workgroup in chunks of 256);
+  //  * rows between 1 and 4 KiB that are not powers of two: as many whole
+  //    rows as fit in 6 KiB per workgroup, chunks of 64 (4000-byte rows 6 %,
+  //    2560- and 3072-byte rows 1-2 % faster than the earlier shapes);
+  //  * shorter rows, and 1 KiB and 2 KiB rows: 4 KiB tiles of whole rows on
+  //    128 threads in natural order.
+  // Units under 16 bytes: 256 threads, 8 KiB tiles, chunks of 64.  Every
+  // field can be overridden per route for sweeps; a tile size below the row
+  // size cuts rows into slices.
+  const bool pow2 = (row_bytes & (row_bytes - 1)) == 0;
+  const bool page_rows = unit == 16 && row_bytes % 4096 == 0;
+  const bool wide_rows = unit == 16 && row_bytes > 4096 && !page_rows;
+  const bool kib_rows = unit == 16 && row_bytes > 1024 && row_bytes < 4096 && !pow2;
+  const bool shaped = page_rows || wide_rows || kib_rows;
+  int64_t auto_tile = unit == 16 ? 4096 : unit_tile_bytes;
+  if (wide_rows) {
+    const int64_t parts = (row_bytes + 6143) / 6144;
+    auto_tile = (row_bytes + parts - 1) / parts;
+  } else if (kib_rows) {
+    auto_tile = (6144 / row_bytes) * row_bytes;
+  }
+  const int64_t tile_bytes = cfg.tile_bytes > 0 ? cfg.tile_bytes : auto_tile;
+  const int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 ? (shaped ? 256 : 128) : 256);
   int64_t chunk = cfg.tile_order > 0
                       ? cfg.tile_order
-                      : (kib_rows ? (kib_lines ? 128 : 64) : (big_rows ? 64 : (mid_rows ? 256 : (unit == 16 ? 1 : 64))));
+                      : (page_rows ? 256 : (shaped ? 64 : (unit == 16 ? 1 : 64)));
 
-  int64_t tile_rows = cfg.tile_bytes == 0 && !mid_rows && !big_rows && !kib_rows
-                          ? whole_row_tile(row_bytes, tile_bytes)
-                          : (tile_bytes + row_bytes - 1) / row_bytes;
+  int64_t tile_rows = cfg.tile_bytes == 0 && !shaped ? whole_row_tile(row_bytes, tile_bytes)
+                                                     : (tile_bytes + row_bytes - 1) / row_bytes;
   if (tile_rows < 1) tile_rows = 1;
   if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
   Shape sh;

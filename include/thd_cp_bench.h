@@ -22,18 +22,17 @@ extern "C" {
  * launch-shape sweeps: the results of thd_swap never depend on it.  Setting
  * it while another thread calls thd_swap on the same route is the caller's
  * race, as is rebuilding that route.  A 0 selects the built-in choice for a
- * field.  The built-in shapes, for rows moved in 16-byte units: rows under
- * 1 KiB, and 1 KiB and 2 KiB rows, in tiles of about 4 KiB of whole rows (a
- * multiple of 128 bytes where one fits) on 128 threads in natural order;
- * other 1-4 KiB rows made of whole 128-byte lines in tiles of at least 4 KiB
- * on 256 threads, chunks of 128; the remaining 1-4 KiB rows one row per
- * 128-thread workgroup, chunks of 64; rows of 4 KiB up to 8 KiB one row per
- * 256-thread workgroup, chunks of 256; rows of 8 KiB and more in slices of
- * about 4 KiB (whole 128-byte lines where the row is made of them) on 128
- * threads, chunks of 64.  Rows moved in narrower units: 8 KiB tiles on 256
- * threads, chunks of 64.  Rows of one unit (1-16 B) whose typical run is
- * shorter than one such tile (4 KiB for 16-byte rows) take an LDS-staged
- * kernel instead.  Every workgroup copies exactly one tile.
+ * field.  The built-in shapes, for rows moved in 16-byte units: rows of
+ * whole 4 KiB pages (4, 8, 12 KiB, ...) as one 4 KiB slice per 256-thread
+ * workgroup, XCD chunks of 256; other rows above 4 KiB in slices of 4-6 KiB
+ * on 256 threads, chunks of 64; rows between 1 and 4 KiB that are not powers
+ * of two as many whole rows as fit in 6 KiB per 256-thread workgroup, chunks
+ * of 64; shorter rows, and 1 KiB and 2 KiB rows, in tiles of about 4 KiB of
+ * whole rows (a multiple of 128 bytes where one fits) on 128 threads in
+ * natural order.  Rows moved in narrower units: 8 KiB tiles on 256 threads,
+ * chunks of 64.  Rows of one unit (1-16 B) whose typical run is shorter than
+ * one such tile (4 KiB for 16-byte rows) take an LDS-staged kernel instead.
+ * Every workgroup copies exactly one tile.
  *   tile_bytes      output bytes per workgroup tile, rounded up to whole rows;
  *                   with 16-byte units, a value below the row size cuts each
  *                   row into slices of about that size
