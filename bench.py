@@ -622,6 +622,9 @@ def measure(thd, torch, workloads, w, steps, warmup, primary):
     # route build and roll device times: events around single launches
     build_ms = _event_samples(torch, stream, lambda: thd.thd_build_route(h, cu, n_slots, cp, total, sh), 100)
     roll_ms = _event_samples(torch, stream, lambda: roll_on(sh), 100)
+    # the floor those figures sit on: the same events around one launch of a
+    # one-workgroup kernel that moves 16 bytes
+    floor_ms = _event_samples(torch, stream, lambda: thd.thd_copy(x, a, 16, sh), 100)
     # route build: host enqueue time of the build call alone
     torch.cuda.synchronize()
     enq = []
@@ -667,6 +670,7 @@ def measure(thd, torch, workloads, w, steps, warmup, primary):
         "route_build_us": round(float(np.median(build_ms)) * 1e3, 2),
         "route_build_enqueue_us": round(float(np.median(enq)) * 1e6, 2),
         "roll_us": round(float(np.median(roll_ms)) * 1e3, 2),
+        "launch_floor_us": round(float(np.median(floor_ms)) * 1e3, 2),
         "host_syncs": host_syncs,
         "copy_ceiling_gbps": {"dtod_copy": round(swap_bytes / (copy_dtod_ms * 1e-3) / 1e9, 1),
                               "stream_copy": round(swap_bytes / (copy_stream_ms * 1e-3) / 1e9, 1)},
@@ -772,7 +776,7 @@ def main():
         },
     }
     for k in ("swap_us", "swap_gbps", "swap_tokens_per_s", "step_tokens_per_s", "route_build_us",
-              "route_build_enqueue_us", "roll_us", "host_syncs", "swap_us_by_direction", "copy_ceiling_gbps",
+              "route_build_enqueue_us", "roll_us", "launch_floor_us", "host_syncs", "swap_us_by_direction", "copy_ceiling_gbps",
               "swap_over_stream_copy", "stream_gbps", "warm_up"):
         out[k] = head[k]
     out["roofline"] = {

@@ -71,6 +71,33 @@ __device__ T block_exclusive_scan(T v, T* s_wave, T* total) {
   return excl;
 }
 
+// Exclusive prefix sum over a workgroup with one barrier: each wave writes
+// its total into half `parity` of s_wave, and after the barrier every wave
+// reads all the totals and takes its own prefix from a wave scan of them
+// (one DPP row holds up to 16 totals).  Consecutive calls must alternate
+// `parity`: a call writes the half the previous call did not, and the half
+// it reads is written again only two calls later, behind the next call's
+// barrier, which no wave passes before every wave has read this call's
+// totals (the barrier's release waits for the wave's LDS loads).  s_wave is
+// LDS scratch of 2 * (kThreads / 64) elements, used by nothing else.
+template <int kThreads>
+__device__ __forceinline__ int32_t block_exclusive_scan_1b(int32_t v, int32_t* s_wave, int parity,
+                                                           int32_t* total) {
+  constexpr int kWaves = kThreads / 64;
+  static_assert(kWaves <= 16, "the wave totals must fit one DPP row");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int32_t x = wave_inclusive_scan(v, 0, ScanAdd{});
+  int32_t* buf = s_wave + parity * kWaves;
+  if (lane == 63) buf[wave] = x;
+  __syncthreads();
+  const int32_t w = lane < kWaves ? buf[lane] : 0;
+  const int32_t xs = wave_inclusive_scan(w, 0, ScanAdd{});
+  *total = __builtin_amdgcn_readlane(xs, kWaves - 1);
+  const int32_t before = wave > 0 ? __builtin_amdgcn_readlane(xs, wave - 1) : 0;
+  return before + x - v;
+}
+
 // K independent exclusive scans over a workgroup in one pass (one set of
 // barriers): sums when kMax is false, maxima when it is true, with
 // `identity` as the value before thread 0.  excl[k] is thread i's result,

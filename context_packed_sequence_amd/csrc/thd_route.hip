@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
   extern __shared__ int32_t s_dyn[];
   __shared__ int s_wave[kBuildWaves + 1];
+  __shared__ int32_t s_wave2[2 * kBuildWaves];  // the segment passes' double-buffered scan
   __shared__ int s_sev;
   const int tid = threadIdx.x;
   const bool writer = !kFused || blockIdx.x == 0;  // the workgroup that writes the route out
@@ -264,8 +265,9 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     }
     const int count_s = j < n_seg ? cs.pieces - merge_s : 0;
     const int count_t = j < n_seg ? ct.pieces - merge_t : 0;
-    int sum;
-    const int off = block_exclusive_scan<kBuildThreads, int>(count_s | (count_t << 16), s_wave, &sum);
+    int32_t sum;
+    const int32_t off = block_exclusive_scan_1b<kBuildThreads>(count_s | (count_t << 16), s_wave2,
+                                                               (base / kBuildThreads) & 1, &sum);
     if (j < n_seg) {
       const int32_t off_s = off & 0xFFFF, off_t = off >> 16;
       for (int p = 0; p < cs.pieces; ++p) {
