@@ -8,6 +8,7 @@
  *   route build, c->z swap -> the two ranks' zigzag tokens      (§3.5-§3.6)
  *   z->c swap -> the packed stream again
  *   roll in zigzag order -> the ranks' valid masks, 13 in all    (§3.6, §3.8)
+ *   the same pack through thd_pack_noalloc (no workspace argument)
  *
  * Usage: thd_worked_example host   (argument checks only; no GPU needed)
  *        thd_worked_example gpu    (the whole example on device 0)
@@ -51,6 +52,11 @@ static int host_checks(void) {
   CHECK(thd_copy(NULL, NULL, 0, NULL) == THD_OK, "empty copy");
   CHECK(thd_pack_workspace_bytes(-1, 8) == -1, "workspace for a negative batch");
   CHECK(strlen(thd_strerror(THD_ERR_CU_DIVISIBLE)) > 0, "strerror");
+  /* the pack without a workspace refuses a batch past its static scratch on the host */
+  CHECK(thd_pack_noalloc(NULL, 2, 1 << 30, 0, 1, 8, 8, 1, 0, NULL, NULL, NULL, NULL, NULL) == THD_ERR_CAPACITY,
+        "pack_noalloc beyond its scratch");
+  CHECK(thd_pack_noalloc(NULL, -1, 8, 0, 1, 8, 8, 1, 0, NULL, NULL, NULL, NULL, NULL) == THD_ERR_ARG,
+        "pack_noalloc with a negative batch");
   return failures;
 }
 
@@ -117,6 +123,23 @@ static int gpu_example(void) {
 
   HIP_OK(hipMemcpy(h_out, packed, sizeof(h_out), hipMemcpyDeviceToHost));
   for (int i = 0; i < T; ++i) CHECK(h_out[i] == want_tokens[i], "packed[%d] = %c", i, (char)h_out[i]);
+
+  /* the same pack without a workspace argument (the library's static scratch),
+     written over the outputs of the first: the same stream and boundaries */
+  HIP_OK(hipMemset(packed, 0, T * 8));
+  HIP_OK(hipMemset(cu, 0, (MAX_DOCS + 2) * 4));
+  HIP_OK(hipMemset(cu_pad, 0, (MAX_DOCS + 2) * 4));
+  CHECK(thd_pack_noalloc(rows, B, S, '_', 'E', 4, T, MAX_DOCS, 'P', packed, cu, cu_pad, status, stream) == THD_OK,
+        "thd_pack_noalloc");
+  HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipMemcpy(h_status, status, 4, hipMemcpyDeviceToHost));
+  CHECK(h_status[0] == THD_OK, "pack_noalloc status %d", h_status[0]);
+  HIP_OK(hipMemcpy(h_cu, cu, sizeof(h_cu), hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(h_cu_pad, cu_pad, sizeof(h_cu_pad), hipMemcpyDeviceToHost));
+  for (int k = 0; k < 4; ++k)
+    CHECK(h_cu[k] == want_cu[k] && h_cu_pad[k] == want_cu_pad[k], "pack_noalloc boundary %d", k);
+  HIP_OK(hipMemcpy(h_out, packed, sizeof(h_out), hipMemcpyDeviceToHost));
+  for (int i = 0; i < T; ++i) CHECK(h_out[i] == want_tokens[i], "pack_noalloc packed[%d] = %c", i, (char)h_out[i]);
   HIP_OK(hipMemcpy(h_out, zig, sizeof(h_out), hipMemcpyDeviceToHost));
   for (int i = 0; i < T; ++i) CHECK(h_out[i] == want_zigzag[i], "zigzag[%d] = %c", i, (char)h_out[i]);
   HIP_OK(hipMemcpy(h_out, back, sizeof(h_out), hipMemcpyDeviceToHost));
