@@ -409,10 +409,10 @@ __global__ __launch_bounds__(kBatchBlock) __attribute__((amdgpu_waves_per_eu(8))
   }
   switch (bt.unit) {
     case 16: swap_tile<u32x4, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
-    case 8: swap_tile<u32x2, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
-    case 4: swap_tile<uint32_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
-    case 2: swap_tile<uint16_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
-    default: swap_tile<uint8_t, kBatchBlock, 8, true, 0>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    case 8: swap_tile<u32x2, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    case 4: swap_tile<uint32_t, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    case 2: swap_tile<uint16_t, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
+    default: swap_tile<uint8_t, kBatchBlock, 8, true>(runs, e, n_runs, bt.in, bt.out, total, bt.row_bytes, r, r1); break;
   }
 }
 
