@@ -493,7 +493,7 @@ def torch_uint8():
     return torch.uint8
 
 
-def measure(thd, torch, workloads, w, steps, warmup, primary):
+def measure(thd, torch, workloads, w, steps, warmup):
     """One workload: device warm-up, in-run ceilings, W warm-up steps, K timed
     steps, then per-direction swap times, route build and roll latency and the
     no-host-wait check.  Returns the figures and the buffers' handles."""
@@ -710,7 +710,7 @@ def main():
         return
     torch.cuda.set_device(torch.device("cuda", 0))
     w = workloads.make(args.workload)
-    head, ctx = measure(thd, torch, workloads, w, args.steps, args.warmup, primary=True)
+    head, ctx = measure(thd, torch, workloads, w, args.steps, args.warmup)
     print(json.dumps({"progress": f"{w.name} measured", "swap_us": head["swap_us"]}), file=sys.stderr, flush=True)
     next_rows = measure_next(thd, torch, workloads, w, ctx["route"], ctx["x"], ctx["stream"], ctx["step_on"])
 
@@ -728,7 +728,7 @@ def main():
         if name == w.name:
             continue
         wo = workloads.make(name)
-        res, octx = measure(thd, torch, workloads, wo, args.steps, args.warmup, primary=False)
+        res, octx = measure(thd, torch, workloads, wo, args.steps, args.warmup)
         if cpu is not None and name == "long1m":
             # a batch of 16 GiB per swap: the oracle is compared and timed on
             # 256 MiB chunks of the GPU's z->c output

@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import check_route_matches_oracle, dev_i32, dev_i64, expected_route, oracle_source_rows, say
+from gpu_util import check_route_matches_oracle, dev_i32, dev_i64, expected_route, say
 
 pytestmark = pytest.mark.gpu
 
