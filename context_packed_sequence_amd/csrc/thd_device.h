@@ -142,6 +142,34 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
   __syncthreads();
 }
 
+// Stores of streamed data that nothing in the launch reads back: raw buffer
+// stores whose cache-policy operand carries the device-scope coherence bit
+// (SC1) and the non-temporal hint (NT), so each store writes through its
+// XCD's L2 towards memory instead of waiting there to be evicted.  Measured
+// on MI355X (same box, interleaved, after a warm-up): a pure write stream of
+// whole lines ran 3-5 % faster than with non-temporal stores (0.5-8 GiB).  A store that
+// covers part of a 128-byte line reaches memory as a partial-line write, as
+// the L2 no longer merges it with the line's other half: copies with
+// misaligned outputs ran 10-16 % slower this way, and swaps of aligned rows
+// gained under 1 %, so the swap kernels keep non-temporal stores.  The
+// resource covers [base, base + bytes): the hardware drops a store outside
+// it.  `base` must be uniform across the workgroup (the resource lives in
+// scalar registers).
+constexpr int kStreamStorePolicy = 16 | 2;  // policy operand bits: SC0 1, NT 2, SC1 16
+constexpr int kBufferWord3 = 0x00020000;    // resource word 3: 32-bit data format, no index stride
+
+typedef unsigned int StoreW4 __attribute__((ext_vector_type(4)));
+
+struct StreamStore {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ StreamStore(void* base, int32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferWord3)) {}
+  // 16 bytes into word i, byte offset 16 * i
+  __device__ __forceinline__ void operator()(int32_t i, StoreW4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, 16 * i, 0, kStreamStorePolicy);
+  }
+};
+
 // Division of a non-negative int32 by a divisor that is fixed for a whole
 // kernel: one multiply-high, an add and two shifts instead of the integer
 // division sequence.  Round-up method of Granlund and Montgomery ("Division

@@ -57,9 +57,10 @@ int thd_route_launch_shape(thd_route* route, int64_t tile_bytes, int32_t nontemp
  * writes each output byte once.  HBM carries reads and writes over the same
  * channels, so a stream that mixes them (a copy, a swap) cannot move bytes
  * faster than a pure read or a pure write stream; these two passes measure
- * the pure streams.  Both use 16-byte non-temporal accesses, 128-thread
- * workgroups and XCD-chunked tile order, in the shapes that streamed fastest
- * on MI355X (4 KiB tiles for the read pass, 2 KiB for the write pass).
+ * the pure streams, in the shapes that streamed fastest on MI355X: 16-byte
+ * accesses on 128-thread workgroups in XCD-chunked tile order; the read pass
+ * non-temporal loads of 4 KiB tiles, the write pass stores of 2 KiB tiles
+ * that write through L2 to memory.
  *
  * thd_read_stream reads `bytes` bytes of `in` and adds to *count (device
  * uint32, 4-byte aligned, cleared by the caller) the number of 16-byte words

@@ -142,13 +142,28 @@ def test_fuzz_swap_batch(thd):
         route.build(dev_i32(w.cu_padded), cp, total)
         hosts = [np.random.default_rng([912, case, i]).integers(0, 256, (total, rb), dtype=np.uint8)
                  for i, rb in enumerate(rbs)]
-        ins = [torch.from_numpy(h).cuda() for h in hosts]
-        outs = [torch.full_like(t, 0x5A) for t in ins]
+        # every tensor at its own byte offset inside a larger buffer, so the
+        # copy unit and the realigning copy's head and tail vary per tensor;
+        # the bytes around each output must stay untouched
+        in_offs = [int(v) for v in rng.integers(0, 16, n)]
+        out_offs = [int(v) for v in rng.integers(0, 16, n)]
+        ins, outs, out_bufs = [], [], []
+        for h, rb, io, oo in zip(hosts, rbs, in_offs, out_offs):
+            nbytes = total * rb
+            ib = torch.empty(nbytes + 32, dtype=torch.uint8, device="cuda")
+            ib[io:io + nbytes] = torch.from_numpy(h.reshape(-1)).cuda()
+            ins.append(ib[io:io + nbytes].view(total, rb))
+            ob = torch.full((nbytes + 32,), 0x5A, dtype=torch.uint8, device="cuda")
+            out_bufs.append(ob)
+            outs.append(ob[oo:oo + nbytes].view(total, rb))
+        tag += f" offsets in {in_offs} out {out_offs}"
         code = thd.thd_swap_batch(route.handle, thd.Z2C if direction == "z2c" else thd.C2Z, ins, outs, rbs, total)
         assert code == thd.THD_OK, tag
         torch.cuda.synchronize()
-        for i, (h, o) in enumerate(zip(hosts, outs)):
+        for i, (h, o, ob, oo) in enumerate(zip(hosts, outs, out_bufs, out_offs)):
             assert np.array_equal(o.cpu().numpy(), O.swap_rows(h, w.cu_padded, cp, total, direction)), f"{tag} #{i}"
+            b = ob.cpu().numpy()
+            assert (b[:oo] == 0x5A).all() and (b[oo + o.numel():] == 0x5A).all(), f"{tag} #{i} guard"
         route.close()
 
 
