@@ -147,7 +147,8 @@ __device__ void block_exclusive_multi(const int64_t (&v)[K], int64_t identity, i
 // (SC1) and the non-temporal hint (NT), so each store writes through its
 // XCD's L2 towards memory instead of waiting there to be evicted.  Measured
 // on MI355X (same box, interleaved, after a warm-up): a pure write stream of
-// whole lines ran 3-5 % faster than with non-temporal stores (0.5-8 GiB).  A store that
+// whole lines ran 3-5 % faster than with non-temporal stores (0.5-8 GiB),
+// and a plain copy of whole lines 0.8-3 %, so both store this way.  A store that
 // covers part of a 128-byte line reaches memory as a partial-line write, as
 // the L2 no longer merges it with the line's other half: copies with
 // misaligned outputs ran 10-16 % slower this way, and swaps of aligned rows

@@ -322,11 +322,13 @@ int thd_route_info(const thd_route* route, int32_t* cp_size, int64_t* total_toke
 /*
  * thd_copy -- plain streaming copy of `bytes` bytes from `in` to `out`
  * (device pointers, non-overlapping): no route, no permutation.  It moves
- * the bytes in 4 KiB tiles with the same 16-byte non-temporal units as
- * thd_swap, in the launch shape that streams a plain copy fastest (128
- * threads per tile, XCD-chunked order with chunks of 256 tiles), so a
- * swap's bandwidth can be set beside that of a copy of the same bytes in
- * the same run: the ceiling a row permutation is measured against.
+ * the bytes in 4 KiB tiles with the same units and non-temporal loads as
+ * thd_swap, in the form that streams a plain copy fastest on MI355X (16-byte
+ * units: 256 threads per tile, one word per lane, XCD-chunked order with
+ * chunks of 256 tiles, and tiles of whole 128-byte lines stored with the
+ * write-through cache policy), so a swap's bandwidth can be set beside that
+ * of a copy of the same bytes in the same run: the ceiling a row permutation
+ * is measured against.
  * Stream-ordered, one launch; THD_ERR_ARG for a negative size or a null
  * pointer (bytes > 0), THD_ERR_ALIAS for overlapping buffers; 0 bytes is
  * THD_OK with no launch.
