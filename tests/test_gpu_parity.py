@@ -307,12 +307,14 @@ def test_one_unit_rows_with_long_runs(thd, rb):
         route.close()
 
 
-@pytest.mark.parametrize("nbytes,offset", [(1 << 20, 0), (4096 * 37 + 16, 0), (1000, 8), (999, 4), (4098, 2),
-                                           (12345, 1), (3, 0)])
+@pytest.mark.parametrize("nbytes,offset", [(1 << 20, 0), (1 << 20, 16), (4096 * 3 + 128, 0), (4096 * 37 + 16, 0),
+                                           (1000, 8), (999, 4), (4098, 2), (12345, 1), (3, 0)])
 def test_plain_copy(thd, nbytes, offset):
     # The calibration copy: every unit width (16/8/4/2/1 B from the size and
-    # the pointers' alignment) and a ragged last tile; the guard bytes around
-    # the destination must stay untouched.
+    # the pointers' alignment), 16-byte tiles of whole 128-byte lines (stored
+    # through L2) and tiles that are not (an output 16 bytes off a line, a
+    # last tile of one line, a ragged last tile); the guard bytes around the
+    # destination must stay untouched.
     import torch
     g = torch.Generator(device="cuda").manual_seed(nbytes)
     src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda", generator=g)
