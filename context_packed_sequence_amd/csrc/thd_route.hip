@@ -119,6 +119,31 @@ __device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, in
   return lo;
 }
 
+// last_run_at_or_before over two run tables at once, so the two searches'
+// LDS loads are in flight together (on a valid route both tables hold the
+// same number of runs, so both searches take the same steps).  Requires
+// a[0].out <= row and b[0].out <= row.
+__device__ __forceinline__ void last_runs_at_or_before(const RunPair* a, int32_t na, const RunPair* b, int32_t nb,
+                                                       int32_t row, int32_t* ka, int32_t* kb) {
+  int32_t lo_a = 0, hi_a = na, lo_b = 0, hi_b = nb;
+  while (hi_a - lo_a > 1 || hi_b - lo_b > 1) {
+    const bool go_a = hi_a - lo_a > 1, go_b = hi_b - lo_b > 1;
+    const int32_t mid_a = (lo_a + hi_a) >> 1, mid_b = (lo_b + hi_b) >> 1;
+    const int32_t out_a = go_a ? a[mid_a].out : 0;
+    const int32_t out_b = go_b ? b[mid_b].out : 0;
+    if (go_a) {
+      if (out_a <= row) lo_a = mid_a;
+      else hi_a = mid_a;
+    }
+    if (go_b) {
+      if (out_b <= row) lo_b = mid_b;
+      else hi_b = mid_b;
+    }
+  }
+  *ka = lo_a;
+  *kb = lo_b;
+}
+
 // Directory entry of output row `row` (a multiple of kDirBlock) from a run
 // table of one order, given the run k that holds it.
 __device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, int32_t n_runs, int32_t row,
@@ -141,7 +166,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   // kLds: docs[3 * n_slots], split[copies * cp * cp]; kFused adds, 8-byte
   // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
   extern __shared__ int32_t s_dyn[];
-  __shared__ int s_wave[kBuildWaves + 1];
+  __shared__ int32_t s_wave1[2 * kBuildWaves];  // the compaction passes' double-buffered scan
   __shared__ int32_t s_wave2[2 * kBuildWaves];  // the segment passes' double-buffered scan
   __shared__ int s_sev;
   const int tid = threadIdx.x;
@@ -180,8 +205,9 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
       else if (d % two_cp != 0) sev = max(sev, kSevDivisible);
       else len = static_cast<int32_t>(d);
     }
-    int sum;
-    const int off = block_exclusive_scan<kBuildThreads, int>(len > 0 ? 1 : 0, s_wave, &sum);
+    int32_t sum;
+    const int32_t off =
+        block_exclusive_scan_1b<kBuildThreads>(len > 0 ? 1 : 0, s_wave1, (base / kBuildThreads) & 1, &sum);
     if (len > 0) {
       const int32_t k = n_docs + off;
       docs[k] = a;
@@ -309,7 +335,27 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     __syncthreads();
   }
 
-  // ---- 5. integrity: same run count both ways; each rank sends and receives T/cp ----
+  if constexpr (kFused) {
+    // ---- 5. this workgroup's share of the directory, both directions.  It
+    //         is written before the integrity check: a route that fails the
+    //         check gets an error status, and a failed route is never read
+    //         past its status.  The counts are clamped to the LDS tables so
+    //         no search leaves them even then. ----
+    const int32_t nd = min(n_dst, lds_run_cap), ns = min(n_src, lds_run_cap);
+    const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
+    const int32_t b0 = static_cast<int32_t>(min(static_cast<int64_t>(blockIdx.x) * dir_per_group,
+                                                static_cast<int64_t>(n_blocks)));
+    const int32_t b1 = static_cast<int32_t>(min(static_cast<int64_t>(n_blocks), static_cast<int64_t>(b0) + dir_per_group));
+    for (int32_t b = b0 + tid; b < b1; b += kBuildThreads) {
+      const int32_t row = b << kDirShift;
+      int32_t kd, ks;
+      last_runs_at_or_before(l_dst, nd, l_src, ns, row, &kd, &ks);
+      ws.dir_dst[b] = dir_entry(l_dst, kd, nd, row, total);
+      ws.dir_src[b] = dir_entry(l_src, ks, ns, row, total);
+    }
+  }
+
+  // ---- 6. integrity: same run count both ways; each rank sends and receives T/cp ----
   bool bad = overflow || n_src != n_dst;
   for (int i = tid; i < cp; i += kBuildThreads) {
     int64_t row = 0, col = 0;
@@ -337,19 +383,6 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     ws.hdr[kHdrCp] = cp;
     ws.hdr[kHdrTotal] = total;
     ws.hdr[kHdrStatus] = s_sev ? THD_ERR_INTEGRITY : THD_OK;
-  }
-  if constexpr (kFused) {
-    // ---- 6. this workgroup's share of the directory, both directions ----
-    if (s_sev) return;  // a failed route is never read past its status
-    const int32_t n_blocks = (total + kDirBlock - 1) / kDirBlock;
-    const int32_t b0 = static_cast<int32_t>(min(static_cast<int64_t>(blockIdx.x) * dir_per_group,
-                                                static_cast<int64_t>(n_blocks)));
-    const int32_t b1 = static_cast<int32_t>(min(static_cast<int64_t>(n_blocks), static_cast<int64_t>(b0) + dir_per_group));
-    for (int32_t b = b0 + tid; b < b1; b += kBuildThreads) {
-      const int32_t row = b << kDirShift;
-      ws.dir_dst[b] = dir_entry(l_dst, last_run_at_or_before(l_dst, 0, n_dst, row), n_dst, row, total);
-      ws.dir_src[b] = dir_entry(l_src, last_run_at_or_before(l_src, 0, n_src, row), n_src, row, total);
-    }
   }
 }
 
