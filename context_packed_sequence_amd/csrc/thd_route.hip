@@ -272,22 +272,26 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
       const Doc dk = load_doc(docs, cap, k);
       ss = chunk_segment(dk, back ? two_cp - 1 - r : r, cp, share);
       cs = cut_segment(ss, share, div_share);
-      if (rem > 0 && cs.rem != 0) {  // not the first row of a source share, not on a destination border
-        const Doc dp = back ? dk : load_doc(docs, cap, k - 1);
-        const Segment p = chunk_segment(dp, back ? r : two_cp - 1 - r, cp, share);
-        merge_s = (p.tok + p.len == ss.tok) ? 1 : 0;
-      }
+      // Merges, in closed form.  The compacted documents lie end to end
+      // (a_k = a_{k-1} + 2 cp c_{k-1}, every c > 0), so in rank r's share a
+      // back chunk continues the tokens of the front chunk before it only
+      // when r + 1 = 2 cp - 1 - r, i.e. r = cp - 1, and a front chunk those
+      // of the previous document's back chunk (which ends at a_k - r c_{k-1})
+      // only when r = 0.  A segment on a destination border starts a run.
+      if (rem > 0 && cs.rem != 0) merge_s = (back ? r == cp - 1 : r == 0) ? 1 : 0;
       // token order: document-major, then chunk
       const int32_t kt = div_two_cp(j);
       const int32_t q = j - kt * two_cp;
       const Doc dt = load_doc(docs, cap, kt);
       st = chunk_segment(dt, q, cp, share);
       ct = cut_segment(st, share, div_share);
-      if (j > 0 && !(kt == 0 && q < cp) && ct.rem != 0) {
-        const Doc dp = q > 0 ? dt : load_doc(docs, cap, kt - 1);
-        const Segment p = chunk_segment(dp, q > 0 ? q - 1 : two_cp - 1, cp, share);
-        merge_t = (p.src + p.len == st.src) ? 1 : 0;
-      }
+      // In token order chunk q continues the zigzag rows of the chunk before
+      // it only where both sit in one rank's share back to back: chunk cp
+      // after chunk cp - 1 (rank cp - 1, front then back of one document) and
+      // chunk 0 after the previous document's chunk 2 cp - 1 (rank 0, whose
+      // back chunk ends at row a_k / cp).  Any other neighbour lies in another
+      // rank's share or, for two back chunks, c + share rows apart.
+      if (ct.rem != 0) merge_t = (q == cp || (q == 0 && kt > 0)) ? 1 : 0;
     }
     const int count_s = j < n_seg ? cs.pieces - merge_s : 0;
     const int count_t = j < n_seg ? ct.pieces - merge_t : 0;
