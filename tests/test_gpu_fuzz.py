@@ -4,20 +4,24 @@ Many small batches drawn from one seeded generator, each through one device
 call and compared whole with the oracle: cp from 1 to 64, 1-80 documents with
 chunks of 1-64 tokens, empty slots anywhere, rows of 1-10240 bytes at byte
 offsets that force every copy unit (16/8/4/2/1 B), both directions; the same
-under random launch-shape overrides (tile size, workgroup cap, cache policy,
-block size, tile order); several tensors through one launch; label rolls with
+under random launch-shape overrides (tile size, cache policy, block size,
+tile order); several tensors through one launch; label rolls with
 real lengths shorter than the padded ones, in natural and in zigzag order;
 packs of token rows with budgets that fit, that hold too few documents, too
-few tokens, or both; corrupted boundary lists on every route-build path.  Each case is printed before it
+few tokens, or both; corrupted boundary lists on every route-build path; and
+route builds alone, cp up to 1024 and up to ~700 documents, on every build
+path.  Each case is printed before it
 runs, and every assertion names its case.
 """
+
+import os
 
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads as W
-from gpu_util import CODE_OF_KIND, dev_i32, dev_i64, say
+from gpu_util import CODE_OF_KIND, check_route_matches_oracle, dev_i32, dev_i64, oracle_source_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +89,40 @@ def test_fuzz_swap(thd):
 TUNE_TILE = [0, 1, 16, 100, 512, 1000, 4096, 5000, 16384, 65536]
 TUNE_BLOCK = [0, 128, 256, 512, 1024]
 TUNE_ORDER = [0, 1, 2, 5, 64, 128, 100000]
+
+
+def test_fuzz_route_build(thd):
+    # Route builds alone, many of them: cp from 2 to 1024, up to ~700
+    # documents of 2cp-64*2cp tokens and 30 empty slots, so every build path
+    # (one launch in LDS, LDS plus the directory kernel, the workspace in
+    # global memory) is drawn.  Runs in both orders and the split matrix must
+    # equal the oracle's, and a swap of row-stamped 16-byte rows in each
+    # direction must fetch the rows the oracle names.  THD_FUZZ_ROUTES sets
+    # the number of cases (default 300; a one-off run of 20000 passed).
+    import torch
+    n_cases = int(os.environ.get("THD_FUZZ_ROUTES", "300"))
+    rng = np.random.default_rng([W.BASE_SEED, 4242])
+    cps = [2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 64, 128, 256, 512, 1024]
+    for case in range(n_cases):
+        cp = int(rng.choice(cps))
+        docs = int(rng.integers(1, 700))
+        max_chunk = int(rng.choice([1, 2, 3, 8, 16, 64]))
+        while 2 * cp * max_chunk * docs > 600000 and docs > 1:
+            docs = max(1, docs // 2)
+        n_empty = int(rng.integers(0, 30))
+        w = W.random_packed([4243, case], cp, docs, max_chunk, n_empty, row_shape=(16,), row_dtype="uint8")
+        total = w.total
+        tag = f"route case {case}: cp {cp} docs {docs} chunk<={max_chunk} empty {n_empty} T {total}"
+        say(tag)
+        route = thd.Route(max(1, w.n_slots), cp, max(total, 1))
+        route.build(dev_i32(w.cu_padded), cp, total)
+        r = check_route_matches_oracle(route, w.cu_padded, cp, total)
+        if total > 0:
+            x = torch.arange(total, dtype=torch.int64, device="cuda").repeat_interleave(2).view(total, 2)
+            for direction, d in (("z2c", thd.Z2C), ("c2z", thd.C2Z)):
+                got = route.swap(x, d)[:, 0].cpu().numpy()
+                assert np.array_equal(got, oracle_source_rows(r, direction)), f"{tag} {direction}"
+        route.close()
 
 
 def test_fuzz_swap_launch_shapes(thd):
