@@ -176,9 +176,6 @@ int thd_build_route(thd_route* route, const int32_t* cu_seqlens_padded, int32_t 
   if (thdcp::launch_route_build(cu_seqlens_padded, n_slots, cp_size, static_cast<int32_t>(total_tokens), route->dev,
                                 s) != hipSuccess)
     return THD_ERR_HIP;
-  if (!thdcp::route_build_fused(n_slots, cp_size) &&
-      thdcp::launch_route_index(route->dev, static_cast<int32_t>(total_tokens), s) != hipSuccess)
-    return THD_ERR_HIP;
   route->built = 1;
   return THD_OK;
 }

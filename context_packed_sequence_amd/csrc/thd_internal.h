@@ -63,12 +63,11 @@ struct RouteDev {
 };
 
 // Launchers (return hipError_t of the launch).
+// The whole build: runs, split matrix, header and directory (one launch, or
+// a build launch followed by the directory launch).
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total,
                               const RouteDev& ws, hipStream_t stream);
 hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream);
-// True when launch_route_build also writes the directory (one launch), so
-// launch_route_index must not follow it.
-bool route_build_fused(int32_t n_slots, int32_t cp);
 
 // Swap launch overrides of one route; 0 in a field means the built-in choice.
 struct SwapLaunch {

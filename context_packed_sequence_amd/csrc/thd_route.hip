@@ -158,36 +158,17 @@ __device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, in
   return e;
 }
 
-template <bool kLds, bool kFused>
-__global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
-                                                                    int32_t cp, int32_t total, RouteDev ws,
-                                                                    int32_t lds_run_cap, FastDiv div_share,
-                                                                    FastDiv div_two_cp, int32_t dir_per_group) {
-  // kLds: docs[3 * n_slots], split[copies * cp * cp]; kFused adds, 8-byte
-  // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
-  extern __shared__ int32_t s_dyn[];
-  __shared__ int32_t s_wave1[2 * kBuildWaves];  // the compaction passes' double-buffered scan
-  __shared__ int32_t s_wave2[2 * kBuildWaves];  // the segment passes' double-buffered scan
-  __shared__ int s_sev;
+// Phases 1 and 2 of every build, in one pass over the boundaries: each
+// boundary rule is checked (the severity of the worst rule a thread sees goes
+// to *s_sev; precedence start, monotone, total, divisibility) and the
+// non-empty slots go to `docs` as [start | chunk | local offset], `cap`
+// entries per array, placed by a one-barrier scan per 1024 slots.  Every
+// thread of the workgroup calls it; it returns the number of documents.  The
+// caller publishes docs and *s_sev with a barrier.
+__device__ __forceinline__ int32_t compact_documents(const int32_t* __restrict__ cu, int32_t n_slots, int32_t cp,
+                                                     int32_t total, int32_t* docs, int32_t cap, int32_t* s_wave1,
+                                                     int* s_sev) {
   const int tid = threadIdx.x;
-  const bool writer = !kFused || blockIdx.x == 0;  // the workgroup that writes the route out
-  const int32_t cap = kLds ? n_slots : ws.docs_cap;
-  const int32_t cp2 = cp * cp;
-  const int copies = kLds ? split_copies(cp, n_slots) : 1;
-  int32_t* docs = kLds ? s_dyn : ws.docs;
-  int32_t* split = kLds ? s_dyn + 3 * n_slots : ws.split;
-  int32_t* my_split = split + (threadIdx.x & 63) % copies * cp2;  // this lane's copy
-  RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + copies * cp2 + 1) & ~1));
-  RunPair* l_dst = l_src + lds_run_cap;
-
-  if (tid == 0) s_sev = 0;
-  for (int i = tid; i < copies * cp2; i += kBuildThreads) {
-    if constexpr (kLds) split[i] = 0;
-    else __hip_atomic_store(&split[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // ---- 1+2. validate (precedence: start, monotone, total, divisibility) and
-  //           compact the non-empty slots, in one pass over the boundaries ----
   int sev = 0;
   if (tid == 0) {
     if (cu[0] != 0) sev = kSevStart;
@@ -216,18 +197,55 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     }
     n_docs += sum;
   }
-  if (sev) atomicMax(&s_sev, sev);
+  if (sev) atomicMax(s_sev, sev);
+  return n_docs;
+}
+
+// Header of a route whose boundaries failed validation (no runs).
+__device__ __forceinline__ void write_failed_header(const RouteDev& ws, int32_t cp, int32_t total, int sev) {
+  ws.hdr[kHdrRunsSrc] = 0;
+  ws.hdr[kHdrRunsDst] = 0;
+  ws.hdr[kHdrDocs] = 0;
+  ws.hdr[kHdrCp] = cp;
+  ws.hdr[kHdrTotal] = total;
+  ws.hdr[kHdrStatus] = severity_to_code(sev);
+}
+
+template <bool kLds, bool kFused>
+__global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
+                                                                    int32_t cp, int32_t total, RouteDev ws,
+                                                                    int32_t lds_run_cap, FastDiv div_share,
+                                                                    FastDiv div_two_cp, int32_t dir_per_group) {
+  // kLds: docs[3 * n_slots], split[copies * cp * cp]; kFused adds, 8-byte
+  // aligned, runs by zigzag row [lds_run_cap] and runs by token [lds_run_cap]
+  extern __shared__ int32_t s_dyn[];
+  __shared__ int32_t s_wave1[2 * kBuildWaves];  // the compaction passes' double-buffered scan
+  __shared__ int32_t s_wave2[2 * kBuildWaves];  // the segment passes' double-buffered scan
+  __shared__ int s_sev;
+  const int tid = threadIdx.x;
+  const bool writer = !kFused || blockIdx.x == 0;  // the workgroup that writes the route out
+  const int32_t cap = kLds ? n_slots : ws.docs_cap;
+  const int32_t cp2 = cp * cp;
+  const int copies = kLds ? split_copies(cp, n_slots) : 1;
+  int32_t* docs = kLds ? s_dyn : ws.docs;
+  int32_t* split = kLds ? s_dyn + 3 * n_slots : ws.split;
+  int32_t* my_split = split + (threadIdx.x & 63) % copies * cp2;  // this lane's copy
+  RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + copies * cp2 + 1) & ~1));
+  RunPair* l_dst = l_src + lds_run_cap;
+
+  if (tid == 0) s_sev = 0;
+  for (int i = tid; i < copies * cp2; i += kBuildThreads) {
+    if constexpr (kLds) split[i] = 0;
+    else __hip_atomic_store(&split[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- 1+2. validate and compact ----
+  const int32_t two_cp = 2 * cp;
+  const int32_t n_docs = compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev);
   if constexpr (!kLds) __threadfence();  // global path: zeroed split and document list are complete
   __syncthreads();                       // publishes the document list to the whole workgroup
   if (s_sev) {
-    if (tid == 0 && writer) {
-      ws.hdr[kHdrRunsSrc] = 0;
-      ws.hdr[kHdrRunsDst] = 0;
-      ws.hdr[kHdrDocs] = 0;
-      ws.hdr[kHdrCp] = cp;
-      ws.hdr[kHdrTotal] = total;
-      ws.hdr[kHdrStatus] = severity_to_code(s_sev);
-    }
+    if (tid == 0 && writer) write_failed_header(ws, cp, total, s_sev);
     return;
   }
 
@@ -390,6 +408,179 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
   }
 }
 
+// Route build with run slots in closed form, for routes of more than one
+// pass of segments.  With the documents end to end, the runs that the
+// segments before segment j of an order produce number j (one each), less
+// the merges the rules above make among them, plus one for every destination
+// border that falls strictly inside one of them (a second piece) or on the
+// start of one the rules would have merged (a merge that does not happen).
+// The merges before j follow from j alone, and the cp - 1 borders are located
+// once per workgroup, so every thread places the runs of its own segment of
+// each order with no scan over the segments before it, and the segments
+// spread over as many workgroups as they fill.  Workgroup 0 also writes the
+// split matrix, in closed form as well (per destination share, the chunks of
+// the two documents at its ends plus 2 c for every document between them),
+// checks it and writes the header; route_index_kernel writes the directory.
+constexpr int kClosedMaxCp = 64;
+
+// Rule merges among token-order segments before segment (document kt, chunk q):
+// at chunk cp of every document and at chunk 0 of every document after the first.
+__device__ __forceinline__ int32_t merges_before_token_order(int32_t kt, int32_t q, int32_t cp) {
+  return (kt >= 1 ? 2 * kt - 1 : 0) + (kt >= 1 && q > 0 ? 1 : 0) + (q > cp ? 1 : 0);
+}
+
+// Rule merges among zigzag-row-order segments before segment (rank r,
+// position rem): front chunks of documents 1.. on rank 0, back chunks on
+// rank cp - 1.  r == cp stands for the end of the order.
+__device__ __forceinline__ int32_t merges_before_zigzag_order(int32_t r, int32_t rem, int32_t cp, int32_t n_docs) {
+  if (r >= cp) return 2 * n_docs - 1;
+  if (r == 0) return rem >= 1 ? (rem - 1) >> 1 : 0;
+  if (r < cp - 1) return n_docs - 1;
+  return n_docs - 1 + (rem >> 1);
+}
+
+// Last document whose first token is at or before t (docs[0] = 0 <= t).
+__device__ __forceinline__ int32_t doc_at(const int32_t* docs, int32_t n_docs, int32_t t) {
+  int32_t lo = 0, hi = n_docs;
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (docs[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Tokens of rank s's two chunks of document k inside [lo, hi).
+__device__ __forceinline__ int32_t rank_tokens_in(const int32_t* docs, int32_t cap, int32_t k, int32_t s, int32_t cp,
+                                                  int32_t lo, int32_t hi) {
+  const int32_t a = docs[k], c = docs[cap + k];
+  int32_t n = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int32_t x0 = a + (h ? 2 * cp - 1 - s : s) * c;
+    n += max(0, min(x0 + c, hi) - max(x0, lo));
+  }
+  return n;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
+                                                                   int32_t cp, int32_t total, RouteDev ws,
+                                                                   FastDiv div_share, FastDiv div_two_cp) {
+  extern __shared__ int32_t s_dyn[];  // docs [3 * n_slots], then (workgroup 0) split [cp * cp]
+  __shared__ int32_t s_wave1[2 * kBuildWaves];
+  __shared__ int s_sev;
+  __shared__ int32_t s_border_s[kClosedMaxCp], s_border_t[kClosedMaxCp];  // segment of a border that adds a run
+  __shared__ int32_t s_end_doc[kClosedMaxCp + 1];                         // document holding token d * share
+  const int tid = threadIdx.x;
+  const bool writer = blockIdx.x == 0;
+  const int32_t cap = n_slots;
+  int32_t* docs = s_dyn;
+  if (tid == 0) s_sev = 0;
+
+  // ---- 1+2. validate and compact (every workgroup) ----
+  const int32_t n_docs = compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev);
+  __syncthreads();
+  if (s_sev) {
+    if (tid == 0 && writer) write_failed_header(ws, cp, total, s_sev);
+    return;
+  }
+  const int32_t share = total / cp, two_cp = 2 * cp, two_n = 2 * n_docs, n_seg = two_cp * n_docs;
+
+  // ---- 3. the destination borders b * share, b = 1 .. cp-1: the segment
+  //         each falls in, per order, kept where it adds a run ----
+  if (tid < cp - 1) {
+    const int32_t t = (tid + 1) * share;
+    const int32_t k = doc_at(docs, n_docs, t);
+    const int32_t a = docs[k], c = docs[cap + k];
+    const int32_t q = (t - a) / c;
+    const bool inside = t - a != q * c;
+    const bool back = q >= cp;
+    const int32_t r = back ? two_cp - 1 - q : q, rem = 2 * k + (back ? 1 : 0);
+    const bool rule_s = rem > 0 && (back ? r == cp - 1 : r == 0);
+    const bool rule_t = q == cp || (q == 0 && k > 0);
+    s_border_s[tid] = (inside || rule_s) ? r * two_n + rem : INT32_MAX;
+    s_border_t[tid] = (inside || rule_t) ? k * two_cp + q : INT32_MAX;
+  }
+  if (writer && tid <= cp) s_end_doc[tid] = tid < cp ? doc_at(docs, n_docs, tid * share) : n_docs - 1;
+  __syncthreads();
+
+  // ---- 4. this thread's segment of each order ----
+  const int32_t j = static_cast<int32_t>(blockIdx.x) * kBuildThreads + tid;
+  if (j < n_seg) {
+    int32_t add_s = 0, add_t = 0;
+    for (int b = 0; b < cp - 1; ++b) {
+      add_s += s_border_s[b] < j ? 1 : 0;
+      add_t += s_border_t[b] < j ? 1 : 0;
+    }
+    // zigzag-row order: rank-major, then document, then front/back chunk
+    const int32_t r = j / two_n, rem = j - r * two_n;
+    const int32_t k = rem >> 1;
+    const bool back = rem & 1;
+    const Segment ss = chunk_segment(load_doc(docs, cap, k), back ? two_cp - 1 - r : r, cp, share);
+    const Cut cs = cut_segment(ss, share, div_share);
+    const int merge_s = (rem > 0 && cs.rem != 0 && (back ? r == cp - 1 : r == 0)) ? 1 : 0;
+    const int32_t base_s = j - merges_before_zigzag_order(r, rem, cp, n_docs) + add_s;
+    for (int p = merge_s; p < cs.pieces; ++p) {
+      const int32_t ptok = p == 0 ? ss.tok : (cs.first_d + p) * share;
+      const int64_t slot = static_cast<int64_t>(base_s) + p - merge_s;
+      if (slot < ws.run_cap) ws.runs_src[slot] = RunPair{ss.src + (ptok - ss.tok), ptok};
+    }
+    // token order: document-major, then chunk
+    const int32_t kt = div_two_cp(j), q = j - kt * two_cp;
+    const Segment st = chunk_segment(load_doc(docs, cap, kt), q, cp, share);
+    const Cut ct = cut_segment(st, share, div_share);
+    const int merge_t = (ct.rem != 0 && (q == cp || (q == 0 && kt > 0))) ? 1 : 0;
+    const int32_t base_t = j - merges_before_token_order(kt, q, cp) + add_t;
+    for (int p = merge_t; p < ct.pieces; ++p) {
+      const int32_t ptok = p == 0 ? st.tok : (ct.first_d + p) * share;
+      const int64_t slot = static_cast<int64_t>(base_t) + p - merge_t;
+      if (slot < ws.run_cap) ws.runs_dst[slot] = RunPair{ptok, st.src + (ptok - st.tok)};
+    }
+  }
+  if (!writer) return;
+
+  // ---- 5. workgroup 0: totals, split matrix, integrity, header ----
+  int32_t* split = s_dyn + 3 * n_slots;
+  for (int32_t e = tid; e < cp * cp; e += kBuildThreads) {
+    const int32_t src = e / cp, d = e - src * cp;
+    const int32_t lo = d * share, hi = lo + share;
+    const int32_t k0 = s_end_doc[d];
+    const int32_t k1 = d + 1 < cp ? doc_at(docs, n_docs, hi - 1) : n_docs - 1;
+    int32_t v = rank_tokens_in(docs, cap, k0, src, cp, lo, hi);
+    // documents strictly between hold 2 c tokens of every rank; sum of c over
+    // documents before k is a_k / (2 cp)
+    if (k1 > k0) v += rank_tokens_in(docs, cap, k1, src, cp, lo, hi) + 2 * ((docs[k1] - docs[k0 + 1]) / two_cp);
+    split[e] = v;
+    ws.split[e] = v;
+  }
+  __syncthreads();
+  int32_t extra_s = 0, extra_t = 0;
+  for (int b = 0; b < cp - 1; ++b) {
+    extra_s += s_border_s[b] != INT32_MAX ? 1 : 0;
+    extra_t += s_border_t[b] != INT32_MAX ? 1 : 0;
+  }
+  const int64_t n_src = static_cast<int64_t>(n_seg) - merges_before_zigzag_order(cp, 0, cp, n_docs) + extra_s;
+  const int64_t n_dst = static_cast<int64_t>(n_seg) - merges_before_token_order(n_docs, 0, cp) + extra_t;
+  bool bad = n_src != n_dst || n_src > ws.run_cap;
+  for (int i = tid; i < cp; i += kBuildThreads) {
+    int64_t row = 0, col = 0;
+    for (int d = 0; d < cp; ++d) {
+      row += split[i * cp + d];
+      col += split[d * cp + i];
+    }
+    if (row != share || col != share) bad = true;
+  }
+  if (bad) atomicMax(&s_sev, 1);
+  __syncthreads();
+  if (tid == 0) {
+    ws.hdr[kHdrRunsSrc] = static_cast<int32_t>(min(n_src, ws.run_cap));
+    ws.hdr[kHdrRunsDst] = static_cast<int32_t>(min(n_dst, ws.run_cap));
+    ws.hdr[kHdrDocs] = n_docs;
+    ws.hdr[kHdrCp] = cp;
+    ws.hdr[kHdrTotal] = total;
+    ws.hdr[kHdrStatus] = s_sev ? THD_ERR_INTEGRITY : THD_OK;
+  }
+}
+
 // The same search done by one wave: each round, 64 lanes probe 64 evenly
 // spaced runs and a ballot keeps the interval that holds the answer, so a
 // list of up to 4096 runs takes two dependent loads instead of twelve.
@@ -474,16 +665,43 @@ int64_t build_lds_bytes(int32_t n_slots, int32_t cp, bool fused) {
   return 4 * ((words + 1) & ~1LL) + 16 * (2LL * cp * n_slots + cp);
 }
 
+namespace {
+
+// Routes of more than four passes of segments, cp <= kClosedMaxCp and
+// documents plus split matrix in LDS: route_runs_kernel, then
+// route_index_kernel.  The two launches cost about what four passes of the
+// one-launch build do (measured on MI355X: 12.3 against 12.7 us for 3680
+// segments, 13.3 against 19.4 us for 8320).
+constexpr int64_t kClosedMinSegments = 4 * kBuildThreads;
+
+bool route_build_closed(int32_t n_slots, int32_t cp) {
+  const int64_t segments = 2LL * cp * n_slots;
+  return segments > kClosedMinSegments && cp <= kClosedMaxCp &&
+         4 * (3LL * n_slots + static_cast<int64_t>(cp) * cp) <= kBuildLdsBytes;
+}
+
 bool route_build_fused(int32_t n_slots, int32_t cp) {
   const int64_t segments = 2LL * cp * n_slots;
   return segments <= kFusedMaxSegments && build_lds_bytes(n_slots, cp, true) <= kBuildLdsBytes;
 }
+
+}  // namespace
 
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total, const RouteDev& ws,
                               hipStream_t stream) {
   const int64_t lds = build_lds_bytes(n_slots, cp, false);
   const FastDiv div_share = FastDiv::make(total / cp > 0 ? total / cp : 1);
   const FastDiv div_two_cp = FastDiv::make(2 * cp);
+  if (route_build_closed(n_slots, cp)) {
+    const int64_t segments = 2LL * cp * n_slots;
+    const int64_t grid = (segments + kBuildThreads - 1) / kBuildThreads;
+    const size_t lds_closed = static_cast<size_t>(4 * (3LL * n_slots + static_cast<int64_t>(cp) * cp));
+    hipLaunchKernelGGL(route_runs_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBuildThreads), lds_closed, stream,
+                       cu, n_slots, cp, total, ws, div_share, div_two_cp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_route_index(ws, total, stream);
+  }
   if (route_build_fused(n_slots, cp)) {
     const int32_t run_cap = 2 * cp * n_slots + cp;
     const int64_t lds_fused = build_lds_bytes(n_slots, cp, true);
@@ -494,14 +712,17 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
     hipLaunchKernelGGL((route_build_kernel<true, true>), dim3(grid), dim3(kBuildThreads),
                        static_cast<size_t>(lds_fused), stream, cu, n_slots, cp, total, ws, run_cap, div_share,
                        div_two_cp, dir_per_group);
-  } else if (lds <= kBuildLdsBytes) {
+    return hipGetLastError();
+  }
+  if (lds <= kBuildLdsBytes)
     hipLaunchKernelGGL((route_build_kernel<true, false>), dim3(1), dim3(kBuildThreads), static_cast<size_t>(lds),
                        stream, cu, n_slots, cp, total, ws, 0, div_share, div_two_cp, 0);
-  } else {
+  else
     hipLaunchKernelGGL((route_build_kernel<false, false>), dim3(1), dim3(kBuildThreads), 0, stream, cu, n_slots, cp,
                        total, ws, 0, div_share, div_two_cp, 0);
-  }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_route_index(ws, total, stream);
 }
 
 hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream) {

@@ -109,14 +109,16 @@ void thd_route_destroy(thd_route* route);
  * borders and writes the maximal runs (in zigzag-row order and in token
  * order) plus the cp x cp split matrix, then a row directory: for every 16th
  * output row of each direction, the input row feeding it, the end of its run,
- * the run's index and which of the 16 rows start a run.  When 2*cp*n_slots
- * <= 16384 and the route fits in 150 KiB of LDS this is one launch of
- * ceil(total_tokens / 16384) workgroups, at most 512, each building the route
- * in its own LDS and writing an equal share of the directory; larger batches
- * take one
- * single-workgroup build launch (in LDS, or in the route's workspace when
- * LDS is too small) and one grid-wide directory launch.  Results and the
- * status word stay on the device.
+ * the run's index and which of the 16 rows start a run.  Launches, by the
+ * route's size (segments = 2*cp*n_slots): above 4096 segments with cp <= 64
+ * and the documents in LDS, ceil(segments / 1024) workgroups that place
+ * every segment's runs at slots given in closed form, then one grid-wide
+ * directory launch; otherwise, up to 16384 segments when the route fits in
+ * 150 KiB of LDS, one launch of ceil(total_tokens / 16384) workgroups, at
+ * most 512, each building the route in its own LDS and writing an equal share
+ * of the directory; larger routes take one single-workgroup build launch (in
+ * LDS, or in the route's workspace when LDS is too small) and the directory
+ * launch.  Results and the status word stay on the device.
  *
  * cp_size == 1: the route is the identity; nothing is launched and the
  * boundaries are not read (the swap short-circuits for one rank before any

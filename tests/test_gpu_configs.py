@@ -201,17 +201,20 @@ def _many_documents(total, n, align, seed):
     return W.cumulative(lens)
 
 
-def test_route_build_above_the_workgroup_cap(thd):
-    # T = 2**24 over 520 documents at cp 8 (8320 zigzag segments, the
-    # one-launch build): 2**20 directory blocks, more than the capped grid
-    # covers at 1024 per workgroup, so each workgroup writes a larger share.
-    # 16-byte rows with 16-byte tiles make every row its own tile, so every
-    # directory entry is read by the swap; every output row is then compared
-    # with the input row the oracle's zigzag layout names for it (c->z: row i
-    # holds token zigzag[i]; z->c: token g comes from the row holding it).
+@pytest.mark.parametrize("n_docs", [250, 520])
+def test_route_build_above_the_workgroup_cap(thd, n_docs):
+    # T = 2**24 at cp 8 with 2**20 directory blocks.  250 documents (4000
+    # zigzag segments) take the one-launch build, whose grid is capped below
+    # the blocks it would need at 1024 per workgroup, so each workgroup writes
+    # a larger share; 520 documents (8320 segments) take the closed-form runs
+    # and the directory launch.  16-byte rows with 16-byte tiles make every
+    # row its own tile, so every directory entry is read by the swap; every
+    # output row is then compared with the input row the oracle's zigzag
+    # layout names for it (c->z: row i holds token zigzag[i]; z->c: token g
+    # comes from the row holding it).
     import torch
     cp, total = 8, 1 << 24
-    cu = _many_documents(total, 520, 2 * cp, 78)
+    cu = _many_documents(total, n_docs, 2 * cp, 78)
     say("route above the workgroup cap: T", total, "slots", len(cu) - 1)
     route = thd.Route(len(cu) - 1, cp, total)
     route.build(dev_i32(cu), cp, total)
@@ -233,8 +236,9 @@ def test_route_build_above_the_workgroup_cap(thd):
 
 
 def test_maximum_size_route_with_many_documents(thd):
-    # T = 2**31 - 64 tokens over 520 documents at cp 8: the build (one
-    # launch, its grid capped) stays within a few milliseconds, every run
+    # T = 2**31 - 64 tokens over 520 documents at cp 8: the build (runs in
+    # closed form, then the directory launch) stays within a few
+    # milliseconds, every run
     # starts and ends where the oracle's single-token form puts its tokens,
     # and a 1-byte-row swap matches that form on sampled tokens and returns
     # the input on the round trip.

@@ -296,9 +296,9 @@ def test_fuzz_pack(thd):
 def test_fuzz_bad_boundaries(thd):
     # one to three corruptions of a valid boundary list (first boundary,
     # a decrease, the total, a length off the 2*cp grid), with slot counts that
-    # take each build path (one launch, one workgroup in LDS, one workgroup in
-    # global memory): the status is the oracle's first failing rule and no
-    # swap writes anything
+    # take each build path (one launch; closed-form runs then the directory
+    # launch; one workgroup in LDS; one workgroup in global memory): the
+    # status is the oracle's first failing rule and no swap writes anything
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 950])
     for case in range(60):

@@ -19,6 +19,14 @@ oracle's maximal runs of the per-token route (Relax PR #273 §2.1) exactly,
 on random batches and on the corner cases that decide a rule: one-token
 chunks, borders on document and chunk starts, a document longer than a
 share, many empty slots.
+
+For batches of many documents the build places runs without a scan: the
+runs before segment j of an order number j, less the rule merges before it,
+plus every destination border before it that falls inside a segment or on
+the start of one the rules would have merged; and the split matrix follows
+per destination share from the two documents at its ends plus 2 c for every
+document between.  Those formulas, written out here, must match the rules
+segment by segment and the oracle's run count and split matrix.
 """
 
 import numpy as np
@@ -69,6 +77,99 @@ def rule_runs(cu, cp, total):
     return by_src, by_tok
 
 
+def closed_form(cu, cp, total):
+    """The slot formulas of the closed-form build: for segment j of each
+    order, the number of runs the segments before it produce, and the split
+    matrix, from the documents and the cp - 1 destination borders alone."""
+    cu = [int(v) for v in cu]
+    docs = [(cu[i], cu[i + 1] - cu[i]) for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+    n, share, two_cp = len(docs), total // cp, 2 * cp
+    a = [start for start, _ in docs]
+    c = [length // two_cp for _, length in docs]
+
+    def doc_at(t):
+        return max(k for k in range(n) if a[k] <= t)
+
+    # each border that adds a run: inside a segment (a second piece), or on the
+    # start of a segment the rules would have merged
+    add_s, add_t = [], []
+    for b in range(1, cp):
+        t = b * share
+        k = doc_at(t)
+        q = (t - a[k]) // c[k]
+        inside = t - a[k] != q * c[k]
+        back = q >= cp
+        r, rem = (two_cp - 1 - q if back else q), 2 * k + (1 if back else 0)
+        if inside or (rem > 0 and (r == cp - 1 if back else r == 0)):
+            add_s.append(r * 2 * n + rem)
+        if inside or q == cp or (q == 0 and k > 0):
+            add_t.append(k * two_cp + q)
+
+    def merges_zigzag(j):
+        r, rem = divmod(j, 2 * n)
+        if r >= cp:
+            return 2 * n - 1
+        if r == 0:
+            return (rem - 1) // 2 if rem >= 1 else 0
+        return n - 1 if r < cp - 1 else n - 1 + rem // 2
+
+    def merges_token(j):
+        k, q = divmod(j, two_cp)
+        return (2 * k - 1 if k >= 1 else 0) + (1 if k >= 1 and q > 0 else 0) + (1 if q > cp else 0)
+
+    def runs_before_zigzag(j):
+        return j - merges_zigzag(j) + sum(1 for e in add_s if e < j)
+
+    def runs_before_token(j):
+        return j - merges_token(j) + sum(1 for e in add_t if e < j)
+
+    def rank_tokens_in(k, s, lo, hi):
+        return sum(max(0, min(x + c[k], hi) - max(x, lo)) for x in (a[k] + s * c[k], a[k] + (two_cp - 1 - s) * c[k]))
+
+    split = np.zeros((cp, cp), dtype=np.int64)
+    for d in range(cp):
+        lo, hi = d * share, (d + 1) * share
+        k0, k1 = doc_at(lo), doc_at(hi - 1)
+        for s_ in range(cp):
+            v = rank_tokens_in(k0, s_, lo, hi)
+            if k1 > k0:   # documents between hold 2 c of every rank; a_k / (2 cp) sums c before k
+                v += rank_tokens_in(k1, s_, lo, hi) + 2 * (a[k1] - a[k0 + 1]) // two_cp
+            split[s_, d] = v
+    return n, runs_before_zigzag, runs_before_token, split
+
+
+def check_closed_form(cu, cp, total):
+    n, before_s, before_t, split = closed_form(cu, cp, total)
+    by_src, by_tok = rule_runs(cu, cp, total)
+    route = O.build_route([int(v) for v in cu], cp, total)
+    assert np.array_equal(split, route["split"]), (list(cu), cp)
+    runs = O.canonical_runs(route)
+    # the slot of a segment's first new run is the number of runs before it:
+    # walk the rules segment by segment and compare at every segment
+    cu_l = [int(v) for v in cu]
+    docs = [(cu_l[i], cu_l[i + 1] - cu_l[i]) for i in range(len(cu_l) - 1) if cu_l[i + 1] > cu_l[i]]
+    share, two_cp = total // cp, 2 * cp
+    a = [d[0] for d in docs]
+    c = [d[1] // two_cp for d in docs]
+    count = 0
+    for j in range(two_cp * n):
+        assert before_s(j) == count, (list(cu), cp, "zigzag", j)
+        r, rem = divmod(j, 2 * n)
+        k, h = rem >> 1, rem & 1
+        tok = a[k] + (two_cp - 1 - r if h else r) * c[k]
+        cut = tok % share
+        count += (2 if cut + c[k] > share else 1) - (1 if rem > 0 and cut != 0 and (r == cp - 1 if h else r == 0) else 0)
+    assert before_s(two_cp * n) == count == len(runs) == len(by_src)
+    count = 0
+    for j in range(two_cp * n):
+        assert before_t(j) == count, (list(cu), cp, "token", j)
+        k, q = divmod(j, two_cp)
+        tok = a[k] + q * c[k]
+        cut = tok % share
+        count += (2 if cut + c[k] > share else 1) - (1 if cut != 0 and (q == cp or (q == 0 and k > 0)) else 0)
+    assert before_t(two_cp * n) == count == len(runs) == len(by_tok)
+
+
 def with_lengths(runs, total):
     """(first out, first in) pairs in output order -> (out, in, length)."""
     outs = [o for o, _ in runs] + [total]
@@ -116,3 +217,30 @@ def test_rules_on_the_configured_workloads():
     for name in ("tiny", "gdn128k", "sft", "sft512", "full"):
         w = W.make(name)
         check(w.cu_padded, w.cp, w.total)
+
+
+@pytest.mark.parametrize("cp", [2, 3, 4, 5, 8, 16, 32])
+def test_closed_form_slots_and_split_on_random_batches(cp):
+    # The formulas route_runs_kernel places runs and fills the split matrix
+    # with: runs before every segment of each order equal the running count of
+    # the rules, the totals equal the oracle's run count, and the split
+    # matrix equals the oracle's.
+    rng = np.random.default_rng([W.BASE_SEED, 32, cp])
+    for _ in range(40):
+        n = int(rng.integers(1, 14))
+        lengths = (rng.integers(0, 7, n) * 2 * cp).tolist()
+        if sum(lengths) == 0:
+            lengths[0] = 2 * cp
+        cu = np.concatenate([[0], np.cumsum(lengths)])
+        check_closed_form(cu, cp, int(cu[-1]))
+
+
+@pytest.mark.parametrize("cu,cp", [([0, 4, 8, 16], 2), ([0, 16, 32], 4), ([0, 64], 4), ([0, 8, 72], 4),
+                                   ([0, 24, 24, 48], 3), ([0, 32, 96, 128], 16)])
+def test_closed_form_on_corner_cases(cu, cp):
+    check_closed_form(np.array(cu), cp, cu[-1])
+
+
+def test_closed_form_on_the_many_document_workload():
+    w = W.make("sft512")
+    check_closed_form(w.cu_padded, w.cp, w.total)
