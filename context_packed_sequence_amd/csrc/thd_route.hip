@@ -119,12 +119,12 @@ __device__ __forceinline__ int32_t last_run_at_or_before(const RunPair* runs, in
   return lo;
 }
 
-// last_run_at_or_before over two run tables at once, so the two searches'
-// LDS loads are in flight together (on a valid route both tables hold the
-// same number of runs, so both searches take the same steps).  Requires
-// a[0].out <= row and b[0].out <= row.
-__device__ __forceinline__ void last_runs_at_or_before(const RunPair* a, int32_t na, const RunPair* b, int32_t nb,
-                                                       int32_t row, int32_t* ka, int32_t* kb) {
+// last_run_at_or_before over two run tables at once, row_a in a and row_b
+// in b, so the two searches' LDS loads are in flight together (tables of
+// equal length take the same steps).  Requires a[0].out <= row_a and
+// b[0].out <= row_b when the table is not empty; an empty table gives 0.
+__device__ __forceinline__ void last_runs_at_or_before(const RunPair* a, int32_t na, int32_t row_a, const RunPair* b,
+                                                       int32_t nb, int32_t row_b, int32_t* ka, int32_t* kb) {
   int32_t lo_a = 0, hi_a = na, lo_b = 0, hi_b = nb;
   while (hi_a - lo_a > 1 || hi_b - lo_b > 1) {
     const bool go_a = hi_a - lo_a > 1, go_b = hi_b - lo_b > 1;
@@ -132,11 +132,11 @@ __device__ __forceinline__ void last_runs_at_or_before(const RunPair* a, int32_t
     const int32_t out_a = go_a ? a[mid_a].out : 0;
     const int32_t out_b = go_b ? b[mid_b].out : 0;
     if (go_a) {
-      if (out_a <= row) lo_a = mid_a;
+      if (out_a <= row_a) lo_a = mid_a;
       else hi_a = mid_a;
     }
     if (go_b) {
-      if (out_b <= row) lo_b = mid_b;
+      if (out_b <= row_b) lo_b = mid_b;
       else hi_b = mid_b;
     }
   }
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
     for (int32_t b = b0 + tid; b < b1; b += kBuildThreads) {
       const int32_t row = b << kDirShift;
       int32_t kd, ks;
-      last_runs_at_or_before(l_dst, nd, l_src, ns, row, &kd, &ks);
+      last_runs_at_or_before(l_dst, nd, row, l_src, ns, row, &kd, &ks);
       ws.dir_dst[b] = dir_entry(l_dst, kd, nd, row, total);
       ws.dir_src[b] = dir_entry(l_src, ks, ns, row, total);
     }
@@ -417,10 +417,11 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
 // The merges before j follow from j alone, and the cp - 1 borders are located
 // once per workgroup, so every thread places the runs of its own segment of
 // each order with no scan over the segments before it, and the segments
-// spread over as many workgroups as they fill.  Workgroup 0 also writes the
-// split matrix, in closed form as well (per destination share, the chunks of
-// the two documents at its ends plus 2 c for every document between them),
-// checks it and writes the header; route_index_kernel writes the directory.
+// spread over as many workgroups as they fill.  One more workgroup, with no
+// segments of its own, writes the split matrix, in closed form as well (per
+// destination share, the chunks of the two documents at its ends plus 2 c
+// for every document between them), checks it and writes the header.  The
+// directory comes from the same launch or from route_index_kernel (below).
 constexpr int kClosedMaxCp = 64;
 
 // Rule merges among token-order segments before segment (document kt, chunk q):
@@ -462,18 +463,109 @@ __device__ __forceinline__ int32_t rank_tokens_in(const int32_t* docs, int32_t c
   return n;
 }
 
+// Runs that segment j of each order starts (n = 0, 1 or 2), at their global
+// slots; two named fields rather than an array, so nothing is indexed at run
+// time and the pair stays in registers.
+struct SegmentRuns {
+  RunPair run0, run1;
+  int32_t slot0, slot1;
+  int n;
+};
+
+// The runs a cut segment starts: its first piece unless it merges into the
+// run before, and the piece after a destination border inside it.
+__device__ __forceinline__ SegmentRuns segment_runs(int32_t base, int merge, int pieces, RunPair first,
+                                                    RunPair second) {
+  SegmentRuns out;
+  out.n = 0;
+  out.run0 = first;
+  out.slot0 = base;
+  out.run1 = second;
+  out.slot1 = base + 1 - merge;
+  if (!merge) out.n = 1;
+  if (pieces == 2) {
+    if (merge) {
+      out.run0 = second;
+      out.slot0 = out.slot1;
+    }
+    ++out.n;
+  }
+  return out;
+}
+
+// The border entries of one order that lie before segment j.
+__device__ __forceinline__ int32_t borders_before(const int32_t* s_border, int32_t cp, int32_t j) {
+  int32_t n = 0;
+  for (int b = 0; b < cp - 1; ++b) n += s_border[b] < j ? 1 : 0;
+  return n;
+}
+
+// Segment j of the zigzag-row order (rank r = j / (2 n_docs), then
+// document, then front/back chunk) and the runs it starts.
+__device__ __forceinline__ SegmentRuns zigzag_segment_runs(const int32_t* docs, int32_t cap, int32_t n_docs, int32_t cp,
+                                                           int32_t share, const FastDiv& div_share,
+                                                           const int32_t* s_border, int32_t j) {
+  const int32_t two_n = 2 * n_docs;
+  const int32_t r = j / two_n, rem = j - r * two_n;
+  const int32_t k = rem >> 1;
+  const bool back = rem & 1;
+  const Segment ss = chunk_segment(load_doc(docs, cap, k), back ? 2 * cp - 1 - r : r, cp, share);
+  const Cut cs = cut_segment(ss, share, div_share);
+  const int merge = (rem > 0 && cs.rem != 0 && (back ? r == cp - 1 : r == 0)) ? 1 : 0;
+  const int32_t base = j - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border, cp, j);
+  const int32_t border = (cs.first_d + 1) * share;
+  return segment_runs(base, merge, cs.pieces, RunPair{ss.src, ss.tok}, RunPair{ss.src + (border - ss.tok), border});
+}
+
+// Segment j of the token order (document j / (2 cp), then chunk) and the runs
+// it starts.
+__device__ __forceinline__ SegmentRuns token_segment_runs(const int32_t* docs, int32_t cap, int32_t cp, int32_t share,
+                                                          const FastDiv& div_share, const FastDiv& div_two_cp,
+                                                          const int32_t* s_border, int32_t j) {
+  const int32_t two_cp = 2 * cp;
+  const int32_t kt = div_two_cp(j), q = j - kt * two_cp;
+  const Segment st = chunk_segment(load_doc(docs, cap, kt), q, cp, share);
+  const Cut ct = cut_segment(st, share, div_share);
+  const int merge = (ct.rem != 0 && (q == cp || (q == 0 && kt > 0))) ? 1 : 0;
+  const int32_t base = j - merges_before_token_order(kt, q, cp) + borders_before(s_border, cp, j);
+  const int32_t border = (ct.first_d + 1) * share;
+  return segment_runs(base, merge, ct.pieces, RunPair{st.tok, st.src}, RunPair{border, st.src + (border - st.tok)});
+}
+
+// With kDir, each workgroup also writes the directory rows that start inside
+// its own segments (a contiguous range of output rows in each order).  It
+// keeps the runs of its segments in LDS, with those of the segment before
+// (the run holding its first row may start there: runs never span more than
+// two segments, as no two consecutive segments both merge) and of the
+// kDirLookahead segments after (a 16-row block reaches at most 16 one-row
+// segments further, and the run after the last one starts at most two
+// segments on), so every search, run end and run-start bit comes from the
+// table; entries carry global run indices.
+constexpr int kDirLookahead = 18;
+// own segments per workgroup with kDir, so that they, the one before and the
+// lookahead fill exactly one pass of the workgroup's threads
+constexpr int kDirSegmentsPerGroup = kBuildThreads - 1 - kDirLookahead;
+constexpr int kDirTableRuns = 2 * kBuildThreads;  // at most two runs per segment
+
+template <bool kDir>
 __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
                                                                    int32_t cp, int32_t total, RouteDev ws,
                                                                    FastDiv div_share, FastDiv div_two_cp) {
-  extern __shared__ int32_t s_dyn[];  // docs [3 * n_slots], then (workgroup 0) split [cp * cp]
+  // docs [3 * n_slots], split [cp * cp] (the writer), then, 8-byte aligned
+  // and with kDir, the runs of each order [kDirTableRuns] each
+  extern __shared__ int32_t s_dyn[];
   __shared__ int32_t s_wave1[2 * kBuildWaves];
   __shared__ int s_sev;
   __shared__ int32_t s_border_s[kClosedMaxCp], s_border_t[kClosedMaxCp];  // segment of a border that adds a run
   __shared__ int32_t s_end_doc[kClosedMaxCp + 1];                         // document holding token d * share
   const int tid = threadIdx.x;
-  const bool writer = blockIdx.x == 0;
+  // the last workgroup has no segments of its own: it writes the split
+  // matrix and the header while the others place runs
+  const bool writer = blockIdx.x == gridDim.x - 1;
   const int32_t cap = n_slots;
   int32_t* docs = s_dyn;
+  RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + cp * cp + 1) & ~1));
+  RunPair* l_dst = l_src + kDirTableRuns;
   if (tid == 0) s_sev = 0;
 
   // ---- 1+2. validate and compact (every workgroup) ----
@@ -503,42 +595,90 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
   if (writer && tid <= cp) s_end_doc[tid] = tid < cp ? doc_at(docs, n_docs, tid * share) : n_docs - 1;
   __syncthreads();
 
-  // ---- 4. this thread's segment of each order ----
-  const int32_t j = static_cast<int32_t>(blockIdx.x) * kBuildThreads + tid;
-  if (j < n_seg) {
-    int32_t add_s = 0, add_t = 0;
-    for (int b = 0; b < cp - 1; ++b) {
-      add_s += s_border_s[b] < j ? 1 : 0;
-      add_t += s_border_t[b] < j ? 1 : 0;
+  // ---- 4. this workgroup's segments of each order (with kDir, and the
+  //         neighbours its directory rows need, into LDS) ----
+  constexpr int32_t kOwn = kDir ? kDirSegmentsPerGroup : kBuildThreads;
+  const int32_t j_lo = static_cast<int32_t>(blockIdx.x) * kOwn;
+  const int32_t j_hi = min(n_seg, j_lo + kOwn);
+  const int32_t t_lo = kDir ? max(0, j_lo - 1) : j_lo;
+  const int32_t t_hi = kDir ? min(n_seg, j_hi + kDirLookahead) : j_hi;
+  // global slot of the table's first run, per order
+  int32_t base_s = 0, base_t = 0;
+  if constexpr (kDir) {
+    if (t_lo < n_seg) {
+      const int32_t r = t_lo / two_n, rem = t_lo - r * two_n;
+      base_s = t_lo - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border_s, cp, t_lo);
+      const int32_t kt = div_two_cp(t_lo), q = t_lo - kt * two_cp;
+      base_t = t_lo - merges_before_token_order(kt, q, cp) + borders_before(s_border_t, cp, t_lo);
     }
-    // zigzag-row order: rank-major, then document, then front/back chunk
-    const int32_t r = j / two_n, rem = j - r * two_n;
-    const int32_t k = rem >> 1;
-    const bool back = rem & 1;
-    const Segment ss = chunk_segment(load_doc(docs, cap, k), back ? two_cp - 1 - r : r, cp, share);
-    const Cut cs = cut_segment(ss, share, div_share);
-    const int merge_s = (rem > 0 && cs.rem != 0 && (back ? r == cp - 1 : r == 0)) ? 1 : 0;
-    const int32_t base_s = j - merges_before_zigzag_order(r, rem, cp, n_docs) + add_s;
-    for (int p = merge_s; p < cs.pieces; ++p) {
-      const int32_t ptok = p == 0 ? ss.tok : (cs.first_d + p) * share;
-      const int64_t slot = static_cast<int64_t>(base_s) + p - merge_s;
-      if (slot < ws.run_cap) ws.runs_src[slot] = RunPair{ss.src + (ptok - ss.tok), ptok};
+  }
+  for (int32_t j = t_lo + tid; j < t_hi; j += kBuildThreads) {
+    const bool own = j >= j_lo && j < j_hi;
+    const SegmentRuns zs = zigzag_segment_runs(docs, cap, n_docs, cp, share, div_share, s_border_s, j);
+    const SegmentRuns ts = token_segment_runs(docs, cap, cp, share, div_share, div_two_cp, s_border_t, j);
+    if (own) {
+      if (zs.n > 0 && zs.slot0 < ws.run_cap) ws.runs_src[zs.slot0] = zs.run0;
+      if (zs.n > 1 && zs.slot1 < ws.run_cap) ws.runs_src[zs.slot1] = zs.run1;
+      if (ts.n > 0 && ts.slot0 < ws.run_cap) ws.runs_dst[ts.slot0] = ts.run0;
+      if (ts.n > 1 && ts.slot1 < ws.run_cap) ws.runs_dst[ts.slot1] = ts.run1;
     }
-    // token order: document-major, then chunk
-    const int32_t kt = div_two_cp(j), q = j - kt * two_cp;
-    const Segment st = chunk_segment(load_doc(docs, cap, kt), q, cp, share);
-    const Cut ct = cut_segment(st, share, div_share);
-    const int merge_t = (ct.rem != 0 && (q == cp || (q == 0 && kt > 0))) ? 1 : 0;
-    const int32_t base_t = j - merges_before_token_order(kt, q, cp) + add_t;
-    for (int p = merge_t; p < ct.pieces; ++p) {
-      const int32_t ptok = p == 0 ? st.tok : (ct.first_d + p) * share;
-      const int64_t slot = static_cast<int64_t>(base_t) + p - merge_t;
-      if (slot < ws.run_cap) ws.runs_dst[slot] = RunPair{ptok, st.src + (ptok - st.tok)};
+    if constexpr (kDir) {
+      const int32_t ls0 = zs.slot0 - base_s, ls1 = zs.slot1 - base_s;
+      const int32_t lt0 = ts.slot0 - base_t, lt1 = ts.slot1 - base_t;
+      if (zs.n > 0 && ls0 >= 0 && ls0 < kDirTableRuns) l_src[ls0] = zs.run0;
+      if (zs.n > 1 && ls1 >= 0 && ls1 < kDirTableRuns) l_src[ls1] = zs.run1;
+      if (ts.n > 0 && lt0 >= 0 && lt0 < kDirTableRuns) l_dst[lt0] = ts.run0;
+      if (ts.n > 1 && lt1 >= 0 && lt1 < kDirTableRuns) l_dst[lt1] = ts.run1;
+    }
+  }
+  if constexpr (kDir) {
+    // runs in the tables: the runs before t_hi less those before t_lo
+    int32_t end_s = 0, end_t = 0;
+    if (t_hi < n_seg) {
+      const int32_t r = t_hi / two_n, rem = t_hi - r * two_n;
+      end_s = t_hi - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border_s, cp, t_hi);
+      const int32_t kt = div_two_cp(t_hi), q = t_hi - kt * two_cp;
+      end_t = t_hi - merges_before_token_order(kt, q, cp) + borders_before(s_border_t, cp, t_hi);
+    } else {
+      end_s = n_seg - merges_before_zigzag_order(cp, 0, cp, n_docs) + borders_before(s_border_s, cp, INT32_MAX);
+      end_t = n_seg - merges_before_token_order(n_docs, 0, cp) + borders_before(s_border_t, cp, INT32_MAX);
+    }
+    const int32_t n_ls = min(end_s - base_s, kDirTableRuns), n_lt = min(end_t - base_t, kDirTableRuns);
+    __syncthreads();
+    // ---- 5. the directory rows that start inside this workgroup's segments ----
+    if (j_lo < n_seg) {
+      // first output row of segment j in each order (total past the last)
+      auto first_row_s = [&](int32_t j) -> int32_t {
+        if (j >= n_seg) return total;
+        const int32_t r = j / two_n, rem = j - r * two_n;
+        const Doc d = load_doc(docs, cap, rem >> 1);
+        return r * share + d.off + ((rem & 1) ? d.c : 0);
+      };
+      auto first_row_t = [&](int32_t j) -> int32_t {
+        if (j >= n_seg) return total;
+        const int32_t kt = div_two_cp(j), q = j - kt * two_cp;
+        const Doc d = load_doc(docs, cap, kt);
+        return d.a + q * d.c;
+      };
+      const int32_t s0 = (first_row_s(j_lo) + kDirBlock - 1) >> kDirShift, s1 = (first_row_s(j_hi) + kDirBlock - 1) >> kDirShift;
+      const int32_t d0 = (first_row_t(j_lo) + kDirBlock - 1) >> kDirShift, d1 = (first_row_t(j_hi) + kDirBlock - 1) >> kDirShift;
+      for (int32_t b = s0 + tid; b < s1; b += kBuildThreads) {
+        const int32_t row = b << kDirShift;
+        DirEntry e = dir_entry(l_src, last_run_at_or_before(l_src, 0, n_ls, row), n_ls, row, total);
+        e.run += base_s;
+        ws.dir_src[b] = e;
+      }
+      for (int32_t b = d0 + tid; b < d1; b += kBuildThreads) {
+        const int32_t row = b << kDirShift;
+        DirEntry e = dir_entry(l_dst, last_run_at_or_before(l_dst, 0, n_lt, row), n_lt, row, total);
+        e.run += base_t;
+        ws.dir_dst[b] = e;
+      }
     }
   }
   if (!writer) return;
 
-  // ---- 5. workgroup 0: totals, split matrix, integrity, header ----
+  // ---- 6. the writer workgroup: totals, split matrix, integrity, header ----
   int32_t* split = s_dyn + 3 * n_slots;
   for (int32_t e = tid; e < cp * cp; e += kBuildThreads) {
     const int32_t src = e / cp, d = e - src * cp;
@@ -673,6 +813,7 @@ namespace {
 // one-launch build do (measured on MI355X: 12.3 against 12.7 us for 3680
 // segments, 13.3 against 19.4 us for 8320).
 constexpr int64_t kClosedMinSegments = 4 * kBuildThreads;
+constexpr int64_t kDirBlocksPerGroup = 2048;  // directory rows per workgroup, on average, for the one-launch form
 
 bool route_build_closed(int32_t n_slots, int32_t cp) {
   const int64_t segments = 2LL * cp * n_slots;
@@ -695,9 +836,22 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
   if (route_build_closed(n_slots, cp)) {
     const int64_t segments = 2LL * cp * n_slots;
     const int64_t grid = (segments + kBuildThreads - 1) / kBuildThreads;
-    const size_t lds_closed = static_cast<size_t>(4 * (3LL * n_slots + static_cast<int64_t>(cp) * cp));
-    hipLaunchKernelGGL(route_runs_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBuildThreads), lds_closed, stream,
-                       cu, n_slots, cp, total, ws, div_share, div_two_cp);
+    const int64_t grid_dir = (segments + kDirSegmentsPerGroup - 1) / kDirSegmentsPerGroup;
+    const int64_t words = 3LL * n_slots + static_cast<int64_t>(cp) * cp;
+    const int64_t lds_runs = 4 * words;
+    const int64_t lds_dir = 4 * ((words + 1) & ~1LL) + 2LL * kDirTableRuns * static_cast<int64_t>(sizeof(RunPair));
+    const int64_t n_blocks = (static_cast<int64_t>(total) + kDirBlock - 1) / kDirBlock;
+    // the directory in the same launch while the rows it spreads over each
+    // workgroup's segments stay few; past that the directory launch spreads
+    // them over the whole chip
+    // one more workgroup than the segments fill: the writer
+    if (n_blocks <= kDirBlocksPerGroup * grid_dir && lds_dir <= kBuildLdsBytes) {
+      hipLaunchKernelGGL((route_runs_kernel<true>), dim3(static_cast<unsigned>(grid_dir + 1)), dim3(kBuildThreads),
+                         static_cast<size_t>(lds_dir), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((route_runs_kernel<false>), dim3(static_cast<unsigned>(grid + 1)), dim3(kBuildThreads),
+                       static_cast<size_t>(lds_runs), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_route_index(ws, total, stream);
