@@ -64,7 +64,8 @@ struct RouteDev {
 
 // Launchers (return hipError_t of the launch).
 // The whole build: runs, split matrix, header and directory (one launch, or
-// a build launch followed by the directory launch).
+// a build launch followed by the directory launch for routes whose
+// directory is too large to write from the build's workgroups).
 hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, int32_t total,
                               const RouteDev& ws, hipStream_t stream);
 hipError_t launch_route_index(const RouteDev& ws, int32_t total, hipStream_t stream);

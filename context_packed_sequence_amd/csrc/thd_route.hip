@@ -808,12 +808,14 @@ int64_t build_lds_bytes(int32_t n_slots, int32_t cp, bool fused) {
 namespace {
 
 // Routes of more than four passes of segments, cp <= kClosedMaxCp and
-// documents plus split matrix in LDS: route_runs_kernel, then
-// route_index_kernel.  The two launches cost about what four passes of the
-// one-launch build do (measured on MI355X: 12.3 against 12.7 us for 3680
-// segments, 13.3 against 19.4 us for 8320).
+// documents plus split matrix in LDS: route_runs_kernel.  Measured on
+// MI355X with the directory in a second launch, the closed form cost about
+// what four passes of the one-pass build do (12.3 against 12.7 us for 3680
+// segments, 13.3 against 19.4 us for 8320); with the directory in the same
+// launch it took 11.5 us for 8320 segments, and 14.0 against 12.6 us for
+// 3680, so the threshold stays at four passes.
 constexpr int64_t kClosedMinSegments = 4 * kBuildThreads;
-constexpr int64_t kDirBlocksPerGroup = 2048;  // directory rows per workgroup, on average, for the one-launch form
+constexpr int64_t kDirBlocksPerGroup = 2048;  // directory entries (16 rows each) per workgroup, on average, for the one-launch form
 
 bool route_build_closed(int32_t n_slots, int32_t cp) {
   const int64_t segments = 2LL * cp * n_slots;
@@ -841,10 +843,10 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
     const int64_t lds_runs = 4 * words;
     const int64_t lds_dir = 4 * ((words + 1) & ~1LL) + 2LL * kDirTableRuns * static_cast<int64_t>(sizeof(RunPair));
     const int64_t n_blocks = (static_cast<int64_t>(total) + kDirBlock - 1) / kDirBlock;
-    // the directory in the same launch while the rows it spreads over each
-    // workgroup's segments stay few; past that the directory launch spreads
-    // them over the whole chip
-    // one more workgroup than the segments fill: the writer
+    // The directory in the same launch while the entries each workgroup's
+    // segments cover stay few; past that the directory launch spreads them
+    // over the whole chip.  One more workgroup than the segments fill: the
+    // writer of the split matrix and header.
     if (n_blocks <= kDirBlocksPerGroup * grid_dir && lds_dir <= kBuildLdsBytes) {
       hipLaunchKernelGGL((route_runs_kernel<true>), dim3(static_cast<unsigned>(grid_dir + 1)), dim3(kBuildThreads),
                          static_cast<size_t>(lds_dir), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp);

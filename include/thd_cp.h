@@ -111,9 +111,13 @@ void thd_route_destroy(thd_route* route);
  * output row of each direction, the input row feeding it, the end of its run,
  * the run's index and which of the 16 rows start a run.  Launches, by the
  * route's size (segments = 2*cp*n_slots): above 4096 segments with cp <= 64
- * and the documents in LDS, ceil(segments / 1024) workgroups that place
- * every segment's runs at slots given in closed form, then one grid-wide
- * directory launch; otherwise, up to 16384 segments when the route fits in
+ * and the documents in LDS, one launch of ceil(segments / 1005) + 1
+ * workgroups that place every segment's runs at slots given in closed form,
+ * each also writing the directory entries whose rows start in its segments
+ * from a copy of their runs in LDS (while the entries of one direction
+ * average at most 2048 per workgroup; past that the directory takes a
+ * second, grid-wide launch);
+ * otherwise, up to 16384 segments when the route fits in
  * 150 KiB of LDS, one launch of ceil(total_tokens / 16384) workgroups, at
  * most 512, each building the route in its own LDS and writing an equal share
  * of the directory; larger routes take one single-workgroup build launch (in
