@@ -94,8 +94,10 @@ TUNE_ORDER = [0, 1, 2, 5, 64, 128, 100000]
 def test_fuzz_route_build(thd):
     # Route builds alone, many of them: cp from 2 to 1024, up to ~700
     # documents of 2cp-64*2cp tokens and 30 empty slots, so every build path
-    # (one launch in LDS, LDS plus the directory kernel, the workspace in
-    # global memory) is drawn.  Runs in both orders and the split matrix must
+    # (run slots in closed form over many workgroups, one launch in LDS, LDS
+    # plus the directory kernel, the workspace in global memory) is drawn;
+    # chunks of one token put the closed form's directory tables at their
+    # reach (a 16-row block spanning 16 one-row segments).  Runs in both orders and the split matrix must
     # equal the oracle's, and a swap of row-stamped 16-byte rows in each
     # direction must fetch the rows the oracle names.  THD_FUZZ_ROUTES sets
     # the number of cases (default 300; a one-off run of 20000 passed).
