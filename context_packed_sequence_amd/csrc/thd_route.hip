@@ -6,9 +6,10 @@
 // contiguous layout, two per document per rank for the zigzag layout -- so the
 // whole exchange is an intersection of intervals instead of per-token index
 // tensors.  The pages do this with Python integers on the host after one
-// device-to-host copy of the boundaries; here it runs on the device (one
-// workgroup, or every workgroup of one launch redundantly when the result
-// fits in LDS), so the host never waits.
+// device-to-host copy of the boundaries; here it runs on the device, so the
+// host never waits: in one workgroup, or in every workgroup of one launch
+// redundantly when the result fits in LDS, or, for routes of many documents,
+// spread over many workgroups that place each segment's runs in closed form.
 //
 // Layout facts used below ("Packed Sequence 与上下文并行" §2.4, §2.5, §3.5):
 //  * a padded document k of length L_k starting at token a_k is cut into 2*cp
@@ -409,15 +410,15 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
 }
 
 // Route build with run slots in closed form, for routes of more than one
-// pass of segments.  With the documents end to end, the runs that the
-// segments before segment j of an order produce number j (one each), less
-// the merges the rules above make among them, plus one for every destination
-// border that falls strictly inside one of them (a second piece) or on the
-// start of one the rules would have merged (a merge that does not happen).
-// The merges before j follow from j alone, and the cp - 1 borders are located
-// once per workgroup, so every thread places the runs of its own segment of
-// each order with no scan over the segments before it, and the segments
-// spread over as many workgroups as they fill.  One more workgroup, with no
+// pass of segments (the threshold is on the host).  With the documents end
+// to end, the runs that the segments before segment j of an order produce
+// number j (one each), less the merges the rules above make among them, plus
+// one for every destination border that falls strictly inside one of them
+// (a second piece) or on the start of one the rules would have merged (a
+// merge that does not happen).  The merges before j follow from j alone, and
+// the cp - 1 borders are located once per workgroup, so every thread places
+// the runs of its own segment of each order with no scan over the segments
+// before it, and the segments spread over many workgroups.  One more workgroup, with no
 // segments of its own, writes the split matrix, in closed form as well (per
 // destination share, the chunks of the two documents at its ends plus 2 c
 // for every document between them), checks it and writes the header.  The
@@ -438,17 +439,6 @@ __device__ __forceinline__ int32_t merges_before_zigzag_order(int32_t r, int32_t
   if (r == 0) return rem >= 1 ? (rem - 1) >> 1 : 0;
   if (r < cp - 1) return n_docs - 1;
   return n_docs - 1 + (rem >> 1);
-}
-
-// Last document whose first token is at or before t (docs[0] = 0 <= t).
-__device__ __forceinline__ int32_t doc_at(const int32_t* docs, int32_t n_docs, int32_t t) {
-  int32_t lo = 0, hi = n_docs;
-  while (hi - lo > 1) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (docs[mid] <= t) lo = mid;
-    else hi = mid;
-  }
-  return lo;
 }
 
 // Tokens of rank s's two chunks of document k inside [lo, hi).
@@ -493,10 +483,17 @@ __device__ __forceinline__ SegmentRuns segment_runs(int32_t base, int merge, int
   return out;
 }
 
-// The border entries of one order that lie before segment j.
+// The border entries of one order that lie before segment j.  The table
+// holds kClosedMaxCp entries (16-byte aligned), those of no border
+// INT32_MAX, so the count runs over whole blocks of 8 entries: two 16-byte
+// LDS reads in flight together instead of a dependent read per border.
 __device__ __forceinline__ int32_t borders_before(const int32_t* s_border, int32_t cp, int32_t j) {
+  const int32_t n_pad = (cp - 1 + 7) & ~7;
   int32_t n = 0;
-  for (int b = 0; b < cp - 1; ++b) n += s_border[b] < j ? 1 : 0;
+  for (int32_t b0 = 0; b0 < n_pad; b0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) n += s_border[b0 + u] < j ? 1 : 0;
+  }
   return n;
 }
 
@@ -542,22 +539,29 @@ __device__ __forceinline__ SegmentRuns token_segment_runs(const int32_t* docs, i
 // segments on), so every search, run end and run-start bit comes from the
 // table; entries carry global run indices.
 constexpr int kDirLookahead = 18;
-// own segments per workgroup with kDir, so that they, the one before and the
-// lookahead fill exactly one pass of the workgroup's threads
-constexpr int kDirSegmentsPerGroup = kBuildThreads - 1 - kDirLookahead;
-constexpr int kDirTableRuns = 2 * kBuildThreads;  // at most two runs per segment
+// Most own segments per workgroup, so that they, the one before and the
+// lookahead fill one pass of the workgroup's threads.
+constexpr int kMaxOwnSegments = kBuildThreads - 1 - kDirLookahead;
+// Runs in each order's LDS table for `own` segments per workgroup: at most
+// two per segment.
+__host__ __device__ inline int32_t dir_table_runs(int32_t own) { return 2 * (own + 1 + kDirLookahead); }
 
+// `own`: segments per workgroup (at most kMaxOwnSegments with kDir, at most
+// kBuildThreads without).
 template <bool kDir>
 __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t* __restrict__ cu, int32_t n_slots,
                                                                    int32_t cp, int32_t total, RouteDev ws,
-                                                                   FastDiv div_share, FastDiv div_two_cp) {
+                                                                   FastDiv div_share, FastDiv div_two_cp,
+                                                                   int32_t own) {
   // docs [3 * n_slots], split [cp * cp] (the writer), then, 8-byte aligned
-  // and with kDir, the runs of each order [kDirTableRuns] each
+  // and with kDir, the runs of each order [dir_table_runs(own)] each
   extern __shared__ int32_t s_dyn[];
   __shared__ int32_t s_wave1[2 * kBuildWaves];
   __shared__ int s_sev;
-  __shared__ int32_t s_border_s[kClosedMaxCp], s_border_t[kClosedMaxCp];  // segment of a border that adds a run
-  __shared__ int32_t s_end_doc[kClosedMaxCp + 1];                         // document holding token d * share
+  // segment of border b + 1 in each order where it adds a run, else INT32_MAX
+  __shared__ __align__(16) int32_t s_border_s[kClosedMaxCp];
+  __shared__ __align__(16) int32_t s_border_t[kClosedMaxCp];
+  __shared__ int32_t s_end_doc[kClosedMaxCp + 1];  // document holding token d * share (the writer)
   const int tid = threadIdx.x;
   // the last workgroup has no segments of its own: it writes the split
   // matrix and the header while the others place runs
@@ -565,8 +569,13 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
   const int32_t cap = n_slots;
   int32_t* docs = s_dyn;
   RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + cp * cp + 1) & ~1));
-  RunPair* l_dst = l_src + kDirTableRuns;
+  const int32_t table_runs = dir_table_runs(own);
+  RunPair* l_dst = l_src + table_runs;
   if (tid == 0) s_sev = 0;
+  if (tid < kClosedMaxCp) {
+    s_border_s[tid] = INT32_MAX;
+    s_border_t[tid] = INT32_MAX;
+  }
 
   // ---- 1+2. validate and compact (every workgroup) ----
   const int32_t n_docs = compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev);
@@ -575,31 +584,41 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
     if (tid == 0 && writer) write_failed_header(ws, cp, total, s_sev);
     return;
   }
+  // valid boundaries and total > 0 (the host's launch condition): n_docs >= 1
   const int32_t share = total / cp, two_cp = 2 * cp, two_n = 2 * n_docs, n_seg = two_cp * n_docs;
 
-  // ---- 3. the destination borders b * share, b = 1 .. cp-1: the segment
-  //         each falls in, per order, kept where it adds a run ----
-  if (tid < cp - 1) {
-    const int32_t t = (tid + 1) * share;
-    const int32_t k = doc_at(docs, n_docs, t);
+  // ---- 3. the destination borders b * share, b = 0 .. cp-1, from the
+  //         document each falls in: the documents lie end to end from token
+  //         0 to T, so the thread of document k takes the borders inside
+  //         [a_k, a_k + 2 cp c_k) and records, per order, the segment of
+  //         each (b >= 1) where it adds a run; the writer also keeps the
+  //         document of every border ----
+  for (int32_t k = tid; k < n_docs; k += kBuildThreads) {
     const int32_t a = docs[k], c = docs[cap + k];
-    const int32_t q = (t - a) / c;
-    const bool inside = t - a != q * c;
-    const bool back = q >= cp;
-    const int32_t r = back ? two_cp - 1 - q : q, rem = 2 * k + (back ? 1 : 0);
-    const bool rule_s = rem > 0 && (back ? r == cp - 1 : r == 0);
-    const bool rule_t = q == cp || (q == 0 && k > 0);
-    s_border_s[tid] = (inside || rule_s) ? r * two_n + rem : INT32_MAX;
-    s_border_t[tid] = (inside || rule_t) ? k * two_cp + q : INT32_MAX;
+    const int32_t end = a + two_cp * c;
+    int32_t b = div_share(a);
+    if (b * share < a) ++b;
+    for (; b < cp && b * share < end; ++b) {
+      if (writer) s_end_doc[b] = k;
+      if (b == 0) continue;
+      const int32_t t = b * share;
+      const int32_t q = (t - a) / c;
+      const bool inside = t - a != q * c;
+      const bool back = q >= cp;
+      const int32_t r = back ? two_cp - 1 - q : q, rem = 2 * k + (back ? 1 : 0);
+      const bool rule_s = rem > 0 && (back ? r == cp - 1 : r == 0);
+      const bool rule_t = q == cp || (q == 0 && k > 0);
+      s_border_s[b - 1] = (inside || rule_s) ? r * two_n + rem : INT32_MAX;
+      s_border_t[b - 1] = (inside || rule_t) ? k * two_cp + q : INT32_MAX;
+    }
   }
-  if (writer && tid <= cp) s_end_doc[tid] = tid < cp ? doc_at(docs, n_docs, tid * share) : n_docs - 1;
+  if (writer && tid == 0) s_end_doc[cp] = n_docs - 1;
   __syncthreads();
 
   // ---- 4. this workgroup's segments of each order (with kDir, and the
   //         neighbours its directory rows need, into LDS) ----
-  constexpr int32_t kOwn = kDir ? kDirSegmentsPerGroup : kBuildThreads;
-  const int32_t j_lo = static_cast<int32_t>(blockIdx.x) * kOwn;
-  const int32_t j_hi = min(n_seg, j_lo + kOwn);
+  const int32_t j_lo = static_cast<int32_t>(min(static_cast<int64_t>(blockIdx.x) * own, static_cast<int64_t>(n_seg)));
+  const int32_t j_hi = min(n_seg, j_lo + own);
   const int32_t t_lo = kDir ? max(0, j_lo - 1) : j_lo;
   const int32_t t_hi = kDir ? min(n_seg, j_hi + kDirLookahead) : j_hi;
   // global slot of the table's first run, per order
@@ -625,10 +644,10 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
     if constexpr (kDir) {
       const int32_t ls0 = zs.slot0 - base_s, ls1 = zs.slot1 - base_s;
       const int32_t lt0 = ts.slot0 - base_t, lt1 = ts.slot1 - base_t;
-      if (zs.n > 0 && ls0 >= 0 && ls0 < kDirTableRuns) l_src[ls0] = zs.run0;
-      if (zs.n > 1 && ls1 >= 0 && ls1 < kDirTableRuns) l_src[ls1] = zs.run1;
-      if (ts.n > 0 && lt0 >= 0 && lt0 < kDirTableRuns) l_dst[lt0] = ts.run0;
-      if (ts.n > 1 && lt1 >= 0 && lt1 < kDirTableRuns) l_dst[lt1] = ts.run1;
+      if (zs.n > 0 && ls0 >= 0 && ls0 < table_runs) l_src[ls0] = zs.run0;
+      if (zs.n > 1 && ls1 >= 0 && ls1 < table_runs) l_src[ls1] = zs.run1;
+      if (ts.n > 0 && lt0 >= 0 && lt0 < table_runs) l_dst[lt0] = ts.run0;
+      if (ts.n > 1 && lt1 >= 0 && lt1 < table_runs) l_dst[lt1] = ts.run1;
     }
   }
   if constexpr (kDir) {
@@ -643,7 +662,7 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
       end_s = n_seg - merges_before_zigzag_order(cp, 0, cp, n_docs) + borders_before(s_border_s, cp, INT32_MAX);
       end_t = n_seg - merges_before_token_order(n_docs, 0, cp) + borders_before(s_border_t, cp, INT32_MAX);
     }
-    const int32_t n_ls = min(end_s - base_s, kDirTableRuns), n_lt = min(end_t - base_t, kDirTableRuns);
+    const int32_t n_ls = min(end_s - base_s, table_runs), n_lt = min(end_t - base_t, table_runs);
     __syncthreads();
     // ---- 5. the directory rows that start inside this workgroup's segments ----
     if (j_lo < n_seg) {
@@ -684,7 +703,10 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
     const int32_t src = e / cp, d = e - src * cp;
     const int32_t lo = d * share, hi = lo + share;
     const int32_t k0 = s_end_doc[d];
-    const int32_t k1 = d + 1 < cp ? doc_at(docs, n_docs, hi - 1) : n_docs - 1;
+    // the document holding token hi - 1: the one holding hi, or the one
+    // before it when hi starts a document (hi > 0 = a_0, so that one exists)
+    const int32_t k_hi = s_end_doc[d + 1];
+    const int32_t k1 = d + 1 < cp ? (docs[k_hi] == hi ? k_hi - 1 : k_hi) : n_docs - 1;
     int32_t v = rank_tokens_in(docs, cap, k0, src, cp, lo, hi);
     // documents strictly between hold 2 c tokens of every rank; sum of c over
     // documents before k is a_k / (2 cp)
@@ -807,19 +829,29 @@ int64_t build_lds_bytes(int32_t n_slots, int32_t cp, bool fused) {
 
 namespace {
 
-// Routes of more than four passes of segments, cp <= kClosedMaxCp and
+// Routes of more than one pass of segments, cp <= kClosedMaxCp and
 // documents plus split matrix in LDS: route_runs_kernel.  Measured on
-// MI355X with the directory in a second launch, the closed form cost about
-// what four passes of the one-pass build do (12.3 against 12.7 us for 3680
-// segments, 13.3 against 19.4 us for 8320); with the directory in the same
-// launch it took 11.5 us for 8320 segments, and 14.0 against 12.6 us for
-// 3680, so the threshold stays at four passes.
-constexpr int64_t kClosedMinSegments = 4 * kBuildThreads;
+// MI355X (same box, interleaved): 7.6 us for 1984 and for 3680 segments
+// against 10.2 and 12.7 us for two and four passes of the one-pass build,
+// 7.9 us for 8320 segments against 19.4 us for nine.
+constexpr int64_t kClosedMinSegments = kBuildThreads;
 constexpr int64_t kDirBlocksPerGroup = 2048;  // directory entries (16 rows each) per workgroup, on average, for the one-launch form
+// Own segments per workgroup of the one-launch form: at least kMinOwnSegments,
+// more once that many would take more than kClosedGroups workgroups (every
+// workgroup validates and compacts the whole boundary list first).  A
+// workgroup's segment and directory work is a chain of dependent LDS reads
+// per thread, so fewer segments per workgroup over more CUs shorten it:
+// 128 segments ran 8320 segments in 9.5 us against 11.5 us with 1005
+// (64: the same, 256: 9.9 us).
+constexpr int64_t kMinOwnSegments = 128;
+constexpr int64_t kClosedGroups = 255;
 
-bool route_build_closed(int32_t n_slots, int32_t cp) {
+// Only for total > 0: valid boundaries then hold at least one document,
+// which the closed form's border and split steps need (an empty batch takes
+// the one-pass build, where it is no work at all).
+bool route_build_closed(int32_t n_slots, int32_t cp, int32_t total) {
   const int64_t segments = 2LL * cp * n_slots;
-  return segments > kClosedMinSegments && cp <= kClosedMaxCp &&
+  return total > 0 && segments > kClosedMinSegments && cp <= kClosedMaxCp &&
          4 * (3LL * n_slots + static_cast<int64_t>(cp) * cp) <= kBuildLdsBytes;
 }
 
@@ -835,13 +867,16 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
   const int64_t lds = build_lds_bytes(n_slots, cp, false);
   const FastDiv div_share = FastDiv::make(total / cp > 0 ? total / cp : 1);
   const FastDiv div_two_cp = FastDiv::make(2 * cp);
-  if (route_build_closed(n_slots, cp)) {
+  if (route_build_closed(n_slots, cp, total)) {
     const int64_t segments = 2LL * cp * n_slots;
     const int64_t grid = (segments + kBuildThreads - 1) / kBuildThreads;
-    const int64_t grid_dir = (segments + kDirSegmentsPerGroup - 1) / kDirSegmentsPerGroup;
+    int64_t own = (segments + kClosedGroups - 1) / kClosedGroups;
+    own = own < kMinOwnSegments ? kMinOwnSegments : (own > kMaxOwnSegments ? kMaxOwnSegments : own);
+    const int64_t grid_dir = (segments + own - 1) / own;
     const int64_t words = 3LL * n_slots + static_cast<int64_t>(cp) * cp;
     const int64_t lds_runs = 4 * words;
-    const int64_t lds_dir = 4 * ((words + 1) & ~1LL) + 2LL * kDirTableRuns * static_cast<int64_t>(sizeof(RunPair));
+    const int64_t lds_dir = 4 * ((words + 1) & ~1LL) +
+                            2LL * dir_table_runs(static_cast<int32_t>(own)) * static_cast<int64_t>(sizeof(RunPair));
     const int64_t n_blocks = (static_cast<int64_t>(total) + kDirBlock - 1) / kDirBlock;
     // The directory in the same launch while the entries each workgroup's
     // segments cover stay few; past that the directory launch spreads them
@@ -849,11 +884,13 @@ hipError_t launch_route_build(const int32_t* cu, int32_t n_slots, int32_t cp, in
     // writer of the split matrix and header.
     if (n_blocks <= kDirBlocksPerGroup * grid_dir && lds_dir <= kBuildLdsBytes) {
       hipLaunchKernelGGL((route_runs_kernel<true>), dim3(static_cast<unsigned>(grid_dir + 1)), dim3(kBuildThreads),
-                         static_cast<size_t>(lds_dir), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp);
+                         static_cast<size_t>(lds_dir), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp,
+                         static_cast<int32_t>(own));
       return hipGetLastError();
     }
     hipLaunchKernelGGL((route_runs_kernel<false>), dim3(static_cast<unsigned>(grid + 1)), dim3(kBuildThreads),
-                       static_cast<size_t>(lds_runs), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp);
+                       static_cast<size_t>(lds_runs), stream, cu, n_slots, cp, total, ws, div_share, div_two_cp,
+                       kBuildThreads);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_route_index(ws, total, stream);

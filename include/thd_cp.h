@@ -110,9 +110,10 @@ void thd_route_destroy(thd_route* route);
  * order) plus the cp x cp split matrix, then a row directory: for every 16th
  * output row of each direction, the input row feeding it, the end of its run,
  * the run's index and which of the 16 rows start a run.  Launches, by the
- * route's size (segments = 2*cp*n_slots): above 4096 segments with cp <= 64
- * and the documents in LDS, one launch of ceil(segments / 1005) + 1
- * workgroups that place every segment's runs at slots given in closed form,
+ * route's size (segments = 2*cp*n_slots): above 1024 segments with cp <= 64
+ * and the documents in LDS, one launch of ceil(segments / own) + 1
+ * workgroups (own = 128 segments each, more when that would take over 255
+ * workgroups) that place every segment's runs at slots given in closed form,
  * each also writing the directory entries whose rows start in its segments
  * from a copy of their runs in LDS (while the entries of one direction
  * average at most 2048 per workgroup; past that the directory takes a

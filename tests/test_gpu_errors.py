@@ -157,6 +157,12 @@ def test_identity_routes(thd):
     assert route.status() == 0
     route.build(dev_i32([0, 0, 0]), 2, 0)            # empty batch
     assert route.status() == 0
+    # an empty batch of many slots (enough segments for the closed-form
+    # build, which needs a document): zero runs, zero split, status OK
+    many = thd.Route(600, 8, 64)
+    many.build(dev_i32([0] * 601), 8, 0)
+    check_route_matches_oracle(many, np.zeros(601, dtype=np.int64), 8, 0)
+    many.close()
     empty = torch.empty(0, 4, dtype=torch.int64, device="cuda")
     assert thd.thd_swap(route.handle, thd.Z2C, empty, torch.empty_like(empty), 0, 32) == thd.THD_IDENTITY
     shifted, mask, status = thd.roll_labels(torch.empty(0, dtype=torch.int64, device="cuda"), dev_i32([0]), None, 2)

@@ -90,12 +90,25 @@ def closed_form(cu, cp, total):
     def doc_at(t):
         return max(k for k in range(n) if a[k] <= t)
 
+    # the document of every border b * share, b = 0 .. cp - 1, as the build
+    # finds it: from each document, the borders inside [a_k, a_k + 2 cp c_k)
+    # (the documents lie end to end, so each border is in exactly one)
+    border_doc = {}
+    for k in range(n):
+        b = -(-a[k] // share)
+        while b < cp and b * share < a[k] + two_cp * c[k]:
+            assert b not in border_doc
+            border_doc[b] = k
+            b += 1
+    assert sorted(border_doc) == list(range(cp))
+    assert all(border_doc[b] == doc_at(b * share) for b in range(cp))
+
     # each border that adds a run: inside a segment (a second piece), or on the
     # start of a segment the rules would have merged
     add_s, add_t = [], []
     for b in range(1, cp):
         t = b * share
-        k = doc_at(t)
+        k = border_doc[b]
         q = (t - a[k]) // c[k]
         inside = t - a[k] != q * c[k]
         back = q >= cp
@@ -129,7 +142,15 @@ def closed_form(cu, cp, total):
     split = np.zeros((cp, cp), dtype=np.int64)
     for d in range(cp):
         lo, hi = d * share, (d + 1) * share
-        k0, k1 = doc_at(lo), doc_at(hi - 1)
+        # the document holding token hi - 1: that of border d + 1, or the one
+        # before it when the border starts a document
+        k0 = border_doc[d]
+        if d + 1 < cp:
+            k_hi = border_doc[d + 1]
+            k1 = k_hi - 1 if a[k_hi] == hi else k_hi
+        else:
+            k1 = n - 1
+        assert (k0, k1) == (doc_at(lo), doc_at(hi - 1))
         for s_ in range(cp):
             v = rank_tokens_in(k0, s_, lo, hi)
             if k1 > k0:   # documents between hold 2 c of every rank; a_k / (2 cp) sums c before k
