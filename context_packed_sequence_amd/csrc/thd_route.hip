@@ -165,10 +165,13 @@ __device__ __forceinline__ DirEntry dir_entry(const RunPair* runs, int32_t k, in
 // non-empty slots go to `docs` as [start | chunk | local offset], `cap`
 // entries per array, placed by a one-barrier scan per 1024 slots.  Every
 // thread of the workgroup calls it; it returns the number of documents.  The
-// caller publishes docs and *s_sev with a barrier.
+// caller publishes docs and *s_sev with a barrier.  on_doc(k, a, len) runs in
+// the thread that places document k (also for boundaries that later fail
+// validation: it must keep its own accesses in bounds).
+template <typename OnDoc>
 __device__ __forceinline__ int32_t compact_documents(const int32_t* __restrict__ cu, int32_t n_slots, int32_t cp,
                                                      int32_t total, int32_t* docs, int32_t cap, int32_t* s_wave1,
-                                                     int* s_sev) {
+                                                     int* s_sev, OnDoc on_doc) {
   const int tid = threadIdx.x;
   int sev = 0;
   if (tid == 0) {
@@ -195,6 +198,7 @@ __device__ __forceinline__ int32_t compact_documents(const int32_t* __restrict__
       docs[k] = a;
       docs[cap + k] = len / two_cp;
       docs[2 * cap + k] = a / cp;
+      on_doc(k, a, len);
     }
     n_docs += sum;
   }
@@ -242,7 +246,8 @@ __global__ __launch_bounds__(kBuildThreads) void route_build_kernel(const int32_
 
   // ---- 1+2. validate and compact ----
   const int32_t two_cp = 2 * cp;
-  const int32_t n_docs = compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev);
+  const int32_t n_docs =
+      compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev, [](int32_t, int32_t, int32_t) {});
   if constexpr (!kLds) __threadfence();  // global path: zeroed split and document list are complete
   __syncthreads();                       // publishes the document list to the whole workgroup
   if (s_sev) {
@@ -483,25 +488,27 @@ __device__ __forceinline__ SegmentRuns segment_runs(int32_t base, int merge, int
   return out;
 }
 
-// The border entries of one order that lie before segment j.  The table
-// holds kClosedMaxCp entries (16-byte aligned), those of no border
-// INT32_MAX, so the count runs over whole blocks of 8 entries: two 16-byte
-// LDS reads in flight together instead of a dependent read per border.
-__device__ __forceinline__ int32_t borders_before(const int32_t* s_border, int32_t cp, int32_t j) {
+// The border entries of one order whose key is below `key` (the key of a
+// segment, in the form the table uses).  The table holds kClosedMaxCp
+// entries (16-byte aligned), those of no border INT32_MAX, so the count runs
+// over whole blocks of 8 entries: two 16-byte LDS reads in flight together
+// instead of a dependent read per border.
+__device__ __forceinline__ int32_t borders_before(const int32_t* s_border, int32_t cp, int32_t key) {
   const int32_t n_pad = (cp - 1 + 7) & ~7;
   int32_t n = 0;
   for (int32_t b0 = 0; b0 < n_pad; b0 += 8) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) n += s_border[b0 + u] < j ? 1 : 0;
+    for (int u = 0; u < 8; ++u) n += s_border[b0 + u] < key ? 1 : 0;
   }
   return n;
 }
 
 // Segment j of the zigzag-row order (rank r = j / (2 n_docs), then
-// document, then front/back chunk) and the runs it starts.
+// document, then front/back chunk) and the runs it starts; its border key is
+// r * zz_stride + rem.
 __device__ __forceinline__ SegmentRuns zigzag_segment_runs(const int32_t* docs, int32_t cap, int32_t n_docs, int32_t cp,
                                                            int32_t share, const FastDiv& div_share,
-                                                           const int32_t* s_border, int32_t j) {
+                                                           const int32_t* s_border, int32_t zz_stride, int32_t j) {
   const int32_t two_n = 2 * n_docs;
   const int32_t r = j / two_n, rem = j - r * two_n;
   const int32_t k = rem >> 1;
@@ -509,7 +516,8 @@ __device__ __forceinline__ SegmentRuns zigzag_segment_runs(const int32_t* docs, 
   const Segment ss = chunk_segment(load_doc(docs, cap, k), back ? 2 * cp - 1 - r : r, cp, share);
   const Cut cs = cut_segment(ss, share, div_share);
   const int merge = (rem > 0 && cs.rem != 0 && (back ? r == cp - 1 : r == 0)) ? 1 : 0;
-  const int32_t base = j - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border, cp, j);
+  const int32_t base =
+      j - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border, cp, r * zz_stride + rem);
   const int32_t border = (cs.first_d + 1) * share;
   return segment_runs(base, merge, cs.pieces, RunPair{ss.src, ss.tok}, RunPair{ss.src + (border - ss.tok), border});
 }
@@ -558,10 +566,14 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
   extern __shared__ int32_t s_dyn[];
   __shared__ int32_t s_wave1[2 * kBuildWaves];
   __shared__ int s_sev;
-  // segment of border b + 1 in each order where it adds a run, else INT32_MAX
+  // Border b + 1's key in each order where it adds a run, else INT32_MAX:
+  // token order, its segment's index; zigzag-row order, r * zz_stride + rem
+  // for its segment (rank r, position rem), with zz_stride = 2 * n_slots >=
+  // 2 * n_docs, so keys sort as the segment indices do while the number of
+  // documents is not yet known.
   __shared__ __align__(16) int32_t s_border_s[kClosedMaxCp];
   __shared__ __align__(16) int32_t s_border_t[kClosedMaxCp];
-  __shared__ int32_t s_end_doc[kClosedMaxCp + 1];  // document holding token d * share (the writer)
+  __shared__ int32_t s_end_doc[kClosedMaxCp];  // document holding token d * share (the writer)
   const int tid = threadIdx.x;
   // the last workgroup has no segments of its own: it writes the split
   // matrix and the header while the others place runs
@@ -571,31 +583,24 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
   RunPair* l_src = reinterpret_cast<RunPair*>(s_dyn + ((3 * n_slots + cp * cp + 1) & ~1));
   const int32_t table_runs = dir_table_runs(own);
   RunPair* l_dst = l_src + table_runs;
+  const int32_t share = total / cp, two_cp = 2 * cp, zz_stride = 2 * n_slots;
   if (tid == 0) s_sev = 0;
   if (tid < kClosedMaxCp) {
     s_border_s[tid] = INT32_MAX;
     s_border_t[tid] = INT32_MAX;
   }
 
-  // ---- 1+2. validate and compact (every workgroup) ----
-  const int32_t n_docs = compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev);
-  __syncthreads();
-  if (s_sev) {
-    if (tid == 0 && writer) write_failed_header(ws, cp, total, s_sev);
-    return;
-  }
-  // valid boundaries and total > 0 (the host's launch condition): n_docs >= 1
-  const int32_t share = total / cp, two_cp = 2 * cp, two_n = 2 * n_docs, n_seg = two_cp * n_docs;
-
-  // ---- 3. the destination borders b * share, b = 0 .. cp-1, from the
-  //         document each falls in: the documents lie end to end from token
-  //         0 to T, so the thread of document k takes the borders inside
-  //         [a_k, a_k + 2 cp c_k) and records, per order, the segment of
-  //         each (b >= 1) where it adds a run; the writer also keeps the
-  //         document of every border ----
-  for (int32_t k = tid; k < n_docs; k += kBuildThreads) {
-    const int32_t a = docs[k], c = docs[cap + k];
-    const int32_t end = a + two_cp * c;
+  // ---- 1+2+3. validate and compact (every workgroup), and the destination
+  //             borders b * share, b = 0 .. cp-1, from the document each
+  //             falls in: the documents lie end to end from token 0 to T, so
+  //             the thread placing document k takes the borders inside
+  //             [a_k, a_k + 2 cp c_k) and records, per order, the key of
+  //             each (b >= 1) where it adds a run; the writer also keeps the
+  //             document of every border.  A document outside [0, T) (only
+  //             on boundaries that fail validation) records nothing. ----
+  auto place_borders = [&](int32_t k, int32_t a, int32_t len) {
+    if (a < 0 || static_cast<int64_t>(a) + len > total) return;
+    const int32_t c = len / two_cp, end = a + len;
     int32_t b = div_share(a);
     if (b * share < a) ++b;
     for (; b < cp && b * share < end; ++b) {
@@ -608,12 +613,18 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
       const int32_t r = back ? two_cp - 1 - q : q, rem = 2 * k + (back ? 1 : 0);
       const bool rule_s = rem > 0 && (back ? r == cp - 1 : r == 0);
       const bool rule_t = q == cp || (q == 0 && k > 0);
-      s_border_s[b - 1] = (inside || rule_s) ? r * two_n + rem : INT32_MAX;
+      s_border_s[b - 1] = (inside || rule_s) ? r * zz_stride + rem : INT32_MAX;
       s_border_t[b - 1] = (inside || rule_t) ? k * two_cp + q : INT32_MAX;
     }
-  }
-  if (writer && tid == 0) s_end_doc[cp] = n_docs - 1;
+  };
+  const int32_t n_docs = compact_documents(cu, n_slots, cp, total, docs, cap, s_wave1, &s_sev, place_borders);
   __syncthreads();
+  if (s_sev) {
+    if (tid == 0 && writer) write_failed_header(ws, cp, total, s_sev);
+    return;
+  }
+  // valid boundaries and total > 0 (the host's launch condition): n_docs >= 1
+  const int32_t two_n = 2 * n_docs, n_seg = two_cp * n_docs;
 
   // ---- 4. this workgroup's segments of each order (with kDir, and the
   //         neighbours its directory rows need, into LDS) ----
@@ -626,14 +637,15 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
   if constexpr (kDir) {
     if (t_lo < n_seg) {
       const int32_t r = t_lo / two_n, rem = t_lo - r * two_n;
-      base_s = t_lo - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border_s, cp, t_lo);
+      base_s = t_lo - merges_before_zigzag_order(r, rem, cp, n_docs) +
+               borders_before(s_border_s, cp, r * zz_stride + rem);
       const int32_t kt = div_two_cp(t_lo), q = t_lo - kt * two_cp;
       base_t = t_lo - merges_before_token_order(kt, q, cp) + borders_before(s_border_t, cp, t_lo);
     }
   }
   for (int32_t j = t_lo + tid; j < t_hi; j += kBuildThreads) {
     const bool own = j >= j_lo && j < j_hi;
-    const SegmentRuns zs = zigzag_segment_runs(docs, cap, n_docs, cp, share, div_share, s_border_s, j);
+    const SegmentRuns zs = zigzag_segment_runs(docs, cap, n_docs, cp, share, div_share, s_border_s, zz_stride, j);
     const SegmentRuns ts = token_segment_runs(docs, cap, cp, share, div_share, div_two_cp, s_border_t, j);
     if (own) {
       if (zs.n > 0 && zs.slot0 < ws.run_cap) ws.runs_src[zs.slot0] = zs.run0;
@@ -655,7 +667,8 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
     int32_t end_s = 0, end_t = 0;
     if (t_hi < n_seg) {
       const int32_t r = t_hi / two_n, rem = t_hi - r * two_n;
-      end_s = t_hi - merges_before_zigzag_order(r, rem, cp, n_docs) + borders_before(s_border_s, cp, t_hi);
+      end_s = t_hi - merges_before_zigzag_order(r, rem, cp, n_docs) +
+              borders_before(s_border_s, cp, r * zz_stride + rem);
       const int32_t kt = div_two_cp(t_hi), q = t_hi - kt * two_cp;
       end_t = t_hi - merges_before_token_order(kt, q, cp) + borders_before(s_border_t, cp, t_hi);
     } else {
@@ -681,17 +694,23 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
       };
       const int32_t s0 = (first_row_s(j_lo) + kDirBlock - 1) >> kDirShift, s1 = (first_row_s(j_hi) + kDirBlock - 1) >> kDirShift;
       const int32_t d0 = (first_row_t(j_lo) + kDirBlock - 1) >> kDirShift, d1 = (first_row_t(j_hi) + kDirBlock - 1) >> kDirShift;
-      for (int32_t b = s0 + tid; b < s1; b += kBuildThreads) {
-        const int32_t row = b << kDirShift;
-        DirEntry e = dir_entry(l_src, last_run_at_or_before(l_src, 0, n_ls, row), n_ls, row, total);
-        e.run += base_s;
-        ws.dir_src[b] = e;
-      }
-      for (int32_t b = d0 + tid; b < d1; b += kBuildThreads) {
-        const int32_t row = b << kDirShift;
-        DirEntry e = dir_entry(l_dst, last_run_at_or_before(l_dst, 0, n_lt, row), n_lt, row, total);
-        e.run += base_t;
-        ws.dir_dst[b] = e;
+      // entry i of each order in one step, both searches' LDS reads in
+      // flight together (an order with no entry i searches an empty table)
+      for (int32_t i = tid; i < max(s1 - s0, d1 - d0); i += kBuildThreads) {
+        const bool has_s = s0 + i < s1, has_t = d0 + i < d1;
+        const int32_t row_s = (s0 + i) << kDirShift, row_t = (d0 + i) << kDirShift;
+        int32_t ks, kt;
+        last_runs_at_or_before(l_src, has_s ? n_ls : 0, row_s, l_dst, has_t ? n_lt : 0, row_t, &ks, &kt);
+        if (has_s) {
+          DirEntry e = dir_entry(l_src, ks, n_ls, row_s, total);
+          e.run += base_s;
+          ws.dir_src[s0 + i] = e;
+        }
+        if (has_t) {
+          DirEntry e = dir_entry(l_dst, kt, n_lt, row_t, total);
+          e.run += base_t;
+          ws.dir_dst[d0 + i] = e;
+        }
       }
     }
   }
@@ -705,8 +724,11 @@ __global__ __launch_bounds__(kBuildThreads) void route_runs_kernel(const int32_t
     const int32_t k0 = s_end_doc[d];
     // the document holding token hi - 1: the one holding hi, or the one
     // before it when hi starts a document (hi > 0 = a_0, so that one exists)
-    const int32_t k_hi = s_end_doc[d + 1];
-    const int32_t k1 = d + 1 < cp ? (docs[k_hi] == hi ? k_hi - 1 : k_hi) : n_docs - 1;
+    int32_t k1 = n_docs - 1;
+    if (d + 1 < cp) {
+      const int32_t k_hi = s_end_doc[d + 1];
+      k1 = docs[k_hi] == hi ? k_hi - 1 : k_hi;
+    }
     int32_t v = rank_tokens_in(docs, cap, k0, src, cp, lo, hi);
     // documents strictly between hold 2 c tokens of every rank; sum of c over
     // documents before k is a_k / (2 cp)

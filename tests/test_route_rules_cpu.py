@@ -159,6 +159,24 @@ def closed_form(cu, cp, total):
     return n, runs_before_zigzag, runs_before_token, split
 
 
+def add_s_list(cu, cp, total):
+    """Zigzag-order segment index r * 2n + rem of every border that adds a run."""
+    cu = [int(v) for v in cu]
+    docs = [(cu[i], cu[i + 1] - cu[i]) for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
+    n, share, two_cp = len(docs), total // cp, 2 * cp
+    out = []
+    for b in range(1, cp):
+        t = b * share
+        k = max(i for i in range(n) if docs[i][0] <= t)
+        a, c = docs[k][0], docs[k][1] // two_cp
+        q = (t - a) // c
+        back = q >= cp
+        r, rem = (two_cp - 1 - q if back else q), 2 * k + (1 if back else 0)
+        if t - a != q * c or (rem > 0 and (r == cp - 1 if back else r == 0)):
+            out.append(r * 2 * n + rem)
+    return out
+
+
 def check_closed_form(cu, cp, total):
     n, before_s, before_t, split = closed_form(cu, cp, total)
     by_src, by_tok = rule_runs(cu, cp, total)
@@ -172,6 +190,14 @@ def check_closed_form(cu, cp, total):
     share, two_cp = total // cp, 2 * cp
     a = [d[0] for d in docs]
     c = [d[1] // two_cp for d in docs]
+    # the build keys zigzag-order borders by r * (2 n_slots) + rem before it
+    # knows n: the same count before every segment as keys r * 2n + rem
+    stride = 2 * (len(cu_l) - 1)
+    add_s_keys = [(e // (2 * n)) * stride + e % (2 * n) for e in add_s_list(cu_l, cp, total)]
+    for j in range(two_cp * n + 1):
+        r, rem = divmod(j, 2 * n)
+        key = r * stride + rem if j < two_cp * n else float("inf")
+        assert sum(1 for e in add_s_keys if e < key) == sum(1 for e in add_s_list(cu_l, cp, total) if e < j)
     count = 0
     for j in range(two_cp * n):
         assert before_s(j) == count, (list(cu), cp, "zigzag", j)
