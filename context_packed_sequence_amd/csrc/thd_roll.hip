@@ -18,6 +18,9 @@
 // ids (plus max_shift tokens of look-ahead) in LDS, then gives each thread one
 // position: a binary search finds the slot, and the J shifted values and J+1
 // mask bytes are written with consecutive lanes on consecutive positions.
+// The ids, and with a route its header and the directory entry of the
+// thread's position, do not depend on the boundaries: they are read in the
+// same memory round trip as the boundaries, before the checks.
 #include "thd_internal.h"
 
 namespace thdcp {
@@ -27,9 +30,9 @@ constexpr int kRollThreads = 256;
 constexpr int kRollLdsSlots = 4096;  // boundaries staged in LDS (dynamic, 8 B per slot, <= 32 KiB)
 
 // Zigzag row of token t from a route's token-order runs (out = token, in =
-// zigzag row) and their directory; every access stays in the run table.
-__device__ __forceinline__ int32_t zigzag_row_of(const RollRoute& rt, int32_t n_runs, int32_t t) {
-  const DirEntry e = rt.dir[t >> kDirShift];
+// zigzag row), given e, the directory entry of t's 16-row block; every access
+// stays in the run table.
+__device__ __forceinline__ int32_t zigzag_row_of(const RollRoute& rt, const DirEntry& e, int32_t n_runs, int32_t t) {
   if (t < e.run_end) return e.in + (t & (kDirBlock - 1));
   const int32_t k = min(run_of_row(e, t), n_runs - 1);
   const RunPair r = rt.runs[k];
@@ -50,6 +53,23 @@ __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __res
   __shared__ int64_t s_ids[kRollThreads + THD_MAX_SHIFT];
   __shared__ int s_sev;
   const int tid = threadIdx.x;
+
+  // reads that do not depend on the boundaries, issued with them
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRollThreads;
+  const int n_load = t0 < total ? static_cast<int>(min(static_cast<int64_t>(total) - t0,
+                                                        static_cast<int64_t>(kRollThreads + max_shift)))
+                                : 0;
+  int64_t id_own = 0, id_ahead = 0;  // ids[t0 + tid] and ids[t0 + kRollThreads + tid]
+  if (tid < n_load) id_own = ids[t0 + tid];
+  if (kRollThreads + tid < n_load) id_ahead = ids[t0 + kRollThreads + tid];
+  const int64_t t = t0 + tid;
+  int32_t route_status = THD_OK, n_runs = 0;
+  DirEntry e_dir{};
+  if constexpr (kRouted) {
+    route_status = rt.hdr[kHdrStatus];
+    n_runs = rt.hdr[kHdrRunsDst];
+    if (t < total) e_dir = rt.dir[t >> kDirShift];
+  }
 
   if (tid == 0) s_sev = 0;
   __syncthreads();
@@ -74,22 +94,15 @@ __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __res
   if (sev) atomicMax(&s_sev, sev);
   __syncthreads();
   int32_t code = severity_to_code(s_sev);
-  int32_t n_runs = 0;
-  if constexpr (kRouted) {
-    const int32_t route_status = rt.hdr[kHdrStatus];
-    if (route_status != THD_OK) code = route_status;  // a failed route build comes first
-    n_runs = rt.hdr[kHdrRunsDst];
-  }
+  if (kRouted && route_status != THD_OK) code = route_status;  // a failed route build comes first
   if (status && blockIdx.x == 0 && tid == 0) *status = code;
   if (code != THD_OK) return;
 
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRollThreads;
   if (t0 >= total) return;
-  const int n_load = static_cast<int>(min(static_cast<int64_t>(total) - t0, static_cast<int64_t>(kRollThreads + max_shift)));
-  for (int i = tid; i < n_load; i += kRollThreads) s_ids[i] = ids[t0 + i];
+  if (tid < n_load) s_ids[tid] = id_own;
+  if (kRollThreads + tid < n_load) s_ids[kRollThreads + tid] = id_ahead;
   __syncthreads();
 
-  const int64_t t = t0 + tid;
   if (t >= total) return;
   // slot s: cu_pad[s] <= t < cu_pad[s + 1]; that slot is never empty
   int32_t lo = 0, hi = n_slots;
@@ -104,7 +117,7 @@ __global__ __launch_bounds__(kRollThreads) void roll_kernel(const int64_t* __res
   else real_len = cu_real ? static_cast<int64_t>(cu_real[lo + 1]) - cu_real[lo]
                           : static_cast<int64_t>(cu_pad[lo + 1]) - cu_pad[lo];
   const int64_t e = static_cast<int64_t>(kLds ? s_pad[lo] : cu_pad[lo]) + real_len;
-  const int64_t row = kRouted ? zigzag_row_of(rt, n_runs, static_cast<int32_t>(t)) : t;
+  const int64_t row = kRouted ? zigzag_row_of(rt, e_dir, n_runs, static_cast<int32_t>(t)) : t;
   mask[row] = t < e ? 1 : 0;
   for (int j = 1; j <= max_shift; ++j) {
     const bool ok = t + j < e;
