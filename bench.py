@@ -233,8 +233,27 @@ def _event_samples(torch, stream, fn, reps):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def _queued_event_samples(torch, stream, fn, reps, hold_cycles=400000):
+    """Device time of fn() in ms when the stream is busy as fn is enqueued,
+    one sample per call: a spin kernel of about 0.2 ms holds the stream while
+    the host records the start event, enqueues fn (which may be several
+    calls, or a graph replay) and records the end event, so the span holds
+    the kernels' dispatch and run, not the host's time to enqueue them."""
+    evs = []
+    for _ in range(reps):
+        a, b = TimingEvent(), TimingEvent()
+        torch.cuda._sleep(hold_cycles)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def _median_event_ms(torch, stream, fn, reps):
-    ts = sorted(_event_samples(torch, stream, fn, reps))
+    """Median device time of fn() queued behind a spin kernel."""
+    ts = sorted(_queued_event_samples(torch, stream, fn, reps))
     return ts[len(ts) // 2]
 
 
@@ -776,7 +795,8 @@ def main():
         },
     }
     for k in ("swap_us", "swap_gbps", "swap_tokens_per_s", "step_tokens_per_s", "route_build_us",
-              "route_build_enqueue_us", "roll_us", "launch_floor_us", "host_syncs", "swap_us_by_direction", "copy_ceiling_gbps",
+              "route_build_enqueue_us", "roll_us", "launch_floor_us", "host_syncs",
+              "swap_us_by_direction", "copy_ceiling_gbps",
               "swap_over_stream_copy", "stream_gbps", "warm_up"):
         out[k] = head[k]
     out["roofline"] = {
