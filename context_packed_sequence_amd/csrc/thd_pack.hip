@@ -254,6 +254,16 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
   __shared__ ChunkPlace s_place;
   const int tid = threadIdx.x;
   const int32_t c = blockIdx.x;
+  // The chunk's tokens do not depend on the scan (only the row's valid end,
+  // applied below, does): they are read first, in the same memory round trip
+  // as the scan's reads.
+  const int32_t b = c < n_chunks ? c / n_ch : 0;
+  const int32_t chunk_start = (c - b * n_ch) * kChunk;
+  const int32_t s0 = chunk_start + tid * kPer;
+  const int64_t* row = tokens + static_cast<int64_t>(b) * seq;
+  int64_t v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) v[i] = c < n_chunks && s0 + i < seq ? row[s0 + i] : 0;
   int64_t used;
   if constexpr (kFused) {
     const PackTotals t =
@@ -267,27 +277,19 @@ __global__ __launch_bounds__(kChunkThreads) void pack_write_kernel(const int64_t
   } else {
     if (ws.hdr[0] != THD_OK) return;  // over budget: nothing is written
     used = ws.hdr[2];
-    if (tid == 0 && c < n_chunks) {
-      const int32_t b = c / n_ch;
+    if (tid == 0 && c < n_chunks)
       s_place = ChunkPlace{ws.ch_prev[c], ws.row_valid[b], ws.ch_doc_base[c], ws.ch_pack_base[c],
                            ws.row_real_off[b]};
-    }
     __syncthreads();
   }
   if (c < n_chunks) {
-    const int32_t b = c / n_ch;
     const int32_t valid_end = s_place.valid_end;
-    const int32_t chunk_start = (c - b * n_ch) * kChunk;
-    const int32_t s0 = chunk_start + tid * kPer;
-    const int64_t* row = tokens + static_cast<int64_t>(b) * seq;
     if (chunk_start < valid_end) {  // uniform per workgroup
-      int64_t v[kPer];
       bool end[kPer];
       int32_t le = 0;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int32_t s = s0 + i;
-        v[i] = s < valid_end ? row[s] : 0;
         end[i] = s < valid_end && (v[i] == eod_id || s + 1 == valid_end);
         if (end[i]) le = s + 1;
       }
