@@ -196,24 +196,28 @@ def _many_documents(total, n, align, seed):
     rng = np.random.default_rng([W.BASE_SEED, seed])
     raw = rng.integers(1, 1000, n).astype(np.float64)
     lens = (np.floor(raw / raw.sum() * total / align) * align).astype(np.int64)
+    lens = np.maximum(lens, align)  # no empty document
     lens[-1] += total - lens.sum()
     assert (lens % align == 0).all() and lens.sum() == total and (lens > 0).all()
     return W.cumulative(lens)
 
 
-@pytest.mark.parametrize("n_docs", [250, 520])
-def test_route_build_above_the_workgroup_cap(thd, n_docs):
-    # T = 2**24 at cp 8 with 2**20 directory blocks.  250 documents (4000
-    # zigzag segments) take the one-launch build, whose grid is capped below
-    # the blocks it would need at 1024 per workgroup, so each workgroup writes
-    # a larger share; 520 documents (8320 segments) take the closed-form runs
-    # and the directory launch.  16-byte rows with 16-byte tiles make every
-    # row its own tile, so every directory entry is read by the swap; every
-    # output row is then compared with the input row the oracle's zigzag
-    # layout names for it (c->z: row i holds token zigzag[i]; z->c: token g
-    # comes from the row holding it).
+@pytest.mark.parametrize("log2_total,n_docs", [(24, 40), (24, 520), (19, 130)])
+def test_route_build_above_the_workgroup_cap(thd, log2_total, n_docs):
+    # cp 8.  T = 2**24 (2**20 directory blocks) over 40 documents (640 zigzag
+    # segments): the one-launch build, whose grid is capped below the blocks
+    # it would need at 1024 per workgroup, so each workgroup writes a larger
+    # share; over 520 documents (8320 segments): the closed-form runs, whose
+    # workgroups would hold over 2048 directory entries each, then the
+    # directory launch.  T = 2**19 over 130 documents (2080 segments, 17
+    # workgroups of 128): the closed-form runs writing about 1900 directory
+    # entries per workgroup in the same launch, two passes of the threads.
+    # 16-byte rows with 16-byte tiles make every row its own tile, so every
+    # directory entry is read by the swap; every output row is then compared
+    # with the input row the oracle's zigzag layout names for it (c->z: row i
+    # holds token zigzag[i]; z->c: token g comes from the row holding it).
     import torch
-    cp, total = 8, 1 << 24
+    cp, total = 8, 1 << log2_total
     cu = _many_documents(total, n_docs, 2 * cp, 78)
     say("route above the workgroup cap: T", total, "slots", len(cu) - 1)
     route = thd.Route(len(cu) - 1, cp, total)

@@ -297,14 +297,15 @@ def test_fuzz_pack(thd):
 
 def test_fuzz_bad_boundaries(thd):
     # one to three corruptions of a valid boundary list (first boundary,
-    # a decrease, the total, a length off the 2*cp grid), with slot counts that
-    # take each build path (one launch; closed-form runs then the directory
-    # launch; one workgroup in LDS; one workgroup in global memory): the
-    # status is the oracle's first failing rule and no swap writes anything
+    # a decrease, the total, a length off the 2*cp grid), with cp and slot
+    # counts that take each build path (one launch; closed-form runs, with or
+    # without the directory launch; one workgroup in LDS, at cp 128; one
+    # workgroup in global memory): the status is the oracle's first failing
+    # rule and no swap writes anything
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 950])
     for case in range(60):
-        cp = int(rng.choice([2, 3, 4, 8, 16, 64]))
+        cp = int(rng.choice([2, 3, 4, 8, 16, 64, 128]))
         n_docs = int(rng.choice([3, 100, 1500, 14000]))
         max_chunk = max(1, min(8, 120000 // (2 * cp * n_docs)))
         w = W.random_packed([951, case], cp, n_docs, max_chunk, int(rng.integers(0, 4)), row_shape=(1,),

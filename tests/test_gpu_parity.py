@@ -239,13 +239,16 @@ def test_worked_example_on_gpu(thd, golden):
 #      directory windows with more runs than the kernel stages in LDS ----
 
 @pytest.mark.parametrize("seed,cp,docs,max_chunk,n_empty", [
-    (200, 2, 7000, 3, 1200),      # many slots, documents still in LDS
+    (200, 2, 7000, 3, 1200),      # many slots, documents still in LDS (the closed form)
     (201, 128, 5, 3, 2),          # cp 128: a 64 KiB split matrix in LDS
-    (202, 2, 3000, 1, 0),         # 4-token documents: thousands of runs per 4096-row window
+    (202, 2, 3000, 1, 0),         # 4-token documents: one-row runs through the closed form's directory tables
     (203, 3, 2500, 1, 40),
-    (204, 2, 14000, 2, 300),      # 3 * n_slots words above the LDS budget: global scratch
+    (204, 2, 14000, 2, 300),      # 3 * n_slots words above the LDS budget: global scratch, then the
+                                  # directory launch with thousands of runs per 4096-row window
     (205, 256, 4, 2, 1),          # cp^2 above the LDS budget: global scratch
     (206, 1024, 3, 2, 1),         # cp at THD_MAX_CP: a 4 MiB split matrix in global scratch
+    (207, 128, 80, 1, 4),         # cp above the closed form's 64, too many segments for the one-launch
+                                  # build: one workgroup with the route in LDS, then the directory launch
 ])
 def test_route_build_slow_paths(thd, seed, cp, docs, max_chunk, n_empty):
     import torch
