@@ -1,8 +1,8 @@
 """Plain CPU oracle for the THD context-parallel layout transform.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the library imports, links or runs this
-package.  The only callers allowed are the test suite, the smoke check in the
-repository's graft entry module and the ``cpu_baseline`` leg of ``bench.py``.
+package.  The only callers allowed are the test suite, ``smoke()`` in
+``__graft_entry__.py`` and the ``cpu_baseline`` leg of ``bench.py``.
 
 The oracle is slow on purpose: it builds per-token index lists, gathers rows with
 ``numpy.take`` on raw bytes and derives labels slot by slot.  It shares no code,
