@@ -249,6 +249,8 @@ def test_worked_example_on_gpu(thd, golden):
     (206, 1024, 3, 2, 1),         # cp at THD_MAX_CP: a 4 MiB split matrix in global scratch
     (207, 128, 80, 1, 4),         # cp above the closed form's 64, too many segments for the one-launch
                                   # build: one workgroup with the route in LDS, then the directory launch
+    (208, 64, 300, 2, 10),        # cp 64, the closed form's largest: 63 borders fill its border tables
+    (209, 65, 300, 1, 3),         # cp 65, just past it: one workgroup with the route in LDS
 ])
 def test_route_build_slow_paths(thd, seed, cp, docs, max_chunk, n_empty):
     import torch
