@@ -263,7 +263,10 @@ int64_t thd_pack_workspace_bytes(int32_t batch, int32_t seq);
  * capacity not a multiple of align, pad_id == eod_id, null pointers,
  * workspace too small),
  * THD_ERR_ALIAS (outputs overlapping each other, the tokens or the workspace).
- * Three kernel launches.
+ * Stream-ordered kernel launches: two for batches of up to 256 chunks of
+ * 1024 tokens (a chunk pass, then a write pass whose every workgroup runs
+ * the scan over all chunks itself), three beyond (a one-workgroup scan
+ * launch between them).
  */
 int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id, int32_t align,
              int64_t capacity, int32_t max_docs, int64_t pad_value, void* workspace, int64_t workspace_bytes,
@@ -289,7 +292,7 @@ int thd_pack(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, 
  * overlaps on one GPU (on different streams, or from different threads,
  * with no ordering between them) race and may produce wrong outputs.
  * Calls ordered on one stream are safe.  Nothing in the scratch has to
- * start at zero.  Stream-ordered, three kernel launches, like thd_pack.
+ * start at zero.  Stream-ordered, the same launches as thd_pack.
  */
 int thd_pack_noalloc(const int64_t* tokens, int32_t batch, int32_t seq, int64_t pad_id, int64_t eod_id,
                      int32_t align, int64_t capacity, int32_t max_docs, int64_t pad_value, int64_t* packed,
