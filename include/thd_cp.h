@@ -216,9 +216,10 @@ int thd_roll_labels(const int64_t* ids, const int32_t* cu_seqlens_padded, const 
  *
  * The route must have been built from the same cu_seqlens_padded and
  * total_tokens (THD_ERR_SHAPE if total_tokens or n_slots differs from the
- * last build's, THD_ERR_NOT_BUILT if never built).  Identity route (cp_size 1): same as thd_roll_labels.  If the
- * route's status is an error, that code is written to `status` and nothing
- * else is written.  Other arguments, errors and outputs as thd_roll_labels.
+ * last build's, THD_ERR_NOT_BUILT if never built).  Identity route (cp_size
+ * 1, or no tokens): same as thd_roll_labels.  If the route's status is an
+ * error, that code is written to `status` and nothing else is written.
+ * Other arguments, errors and outputs as thd_roll_labels.
  */
 int thd_roll_labels_zigzag(const thd_route* route, const int64_t* ids, const int32_t* cu_seqlens_padded,
                            const int32_t* cu_seqlens, int32_t n_slots, int64_t total_tokens, int32_t max_shift,
