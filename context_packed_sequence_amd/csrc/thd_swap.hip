@@ -551,13 +551,14 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
   //  * rows between 1 and 4 KiB that are not powers of two: as many whole
   //    rows as fit in 6 KiB per workgroup, chunks of 64 (4000-byte rows 6 %,
   //    2560- and 3072-byte rows 1-2 % faster than the earlier shapes);
-  //  * shorter rows, and 1 KiB and 2 KiB rows: 4 KiB tiles of whole rows
-  //    (sized to a multiple of 128 bytes where one fits) on 256 threads,
-  //    XCD-chunked order with chunks of 256 tiles (64 for rows under 64
-  //    bytes), where the tile holds at least 240 16-byte words: 0.6-1.4 %
-  //    faster than 128 threads in natural order on 64-2048-byte rows,
-  //    3-5 % on 48- and 80-byte rows (3840-byte tiles), level on 16- and
-  //    32-byte rows; tiles of fewer words keep 128 threads in natural order.
+  //  * shorter rows, and 1 KiB and 2 KiB rows: the most whole rows that fit
+  //    in 4 KiB on 256 threads, XCD-chunked order with chunks of 256 tiles
+  //    (64 for rows under 64 bytes), when those rows hold at least 220
+  //    16-byte words: against 128 threads in natural order with tiles of
+  //    whole 128-byte lines, 0.6-1.4 % faster on 64-2048-byte rows, 2-13 %
+  //    on rows that are not powers of two (272-byte rows 188.5 -> 163.7 us
+  //    per GiB swap), level on 16- and 32-byte rows; rows whose 4 KiB tile
+  //    would hold fewer words keep the whole-line tile (below).
   // Units under 16 bytes: 256 threads, 8 KiB tiles, chunks of 64.  Every
   // field can be overridden per route for sweeps; a tile size below the row
   // size cuts rows into slices.
@@ -578,11 +579,21 @@ hipError_t launch_swap(const int32_t* hdr, const RunPair* runs, int runs_word, c
                                                      : (tile_bytes + row_bytes - 1) / row_bytes;
   if (tile_rows < 1) tile_rows = 1;
   if (tile_rows > (1 << 30)) tile_rows = 1 << 30;
-  // 16-byte rows under 4 KiB take 256 threads in XCD-chunked order when
-  // their whole-row tile fills at least 240 of the 256 lanes' words, else
-  // 128 threads in natural order (400-byte rows: 3200-byte tiles, 2.8 %
-  // slower on 256 threads)
-  const bool full_tile = tile_rows * row_bytes >= 240 * 16;
+  // 16-byte rows under 4 KiB: as many whole rows as fit in 4 KiB when they
+  // fill at least 220 of the 256 lanes' 16-byte words (on 256 threads, up to
+  // 13 % faster than the tile of whole 128-byte lines when that one fills
+  // fewer); otherwise the whole-line tile, on 256 threads in XCD-chunked
+  // order when it fills at least 240 words, else on 128 threads in natural
+  // order (832-byte rows: 3328-byte tiles, 2.4 % slower on 256 threads).
+  bool full_tile = false;
+  if (cfg.tile_bytes == 0 && unit == 16 && !shaped) {
+    const int64_t most = 4096 / row_bytes;
+    if (most >= 1 && most * row_bytes >= 220 * 16) {
+      tile_rows = most;
+      full_tile = true;
+    }
+  }
+  full_tile = full_tile || tile_rows * row_bytes >= 240 * 16;
   int block = cfg.block_threads > 0 ? cfg.block_threads : (unit == 16 && !shaped && !full_tile ? 128 : 256);
   int64_t chunk = cfg.tile_order > 0 ? cfg.tile_order
                   : page_rows        ? 256
