@@ -62,8 +62,8 @@ def parse():
     return p.parse_args()
 
 
-ROW_SWEEP_BYTES = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 64, 100, 128, 256, 512, 1024, 1536, 2048, 2560, 3072,
-                   4000, 4096, 5120, 6144, 8192, 10240, 12288, 14336, 16384, 65536)
+ROW_SWEEP_BYTES = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 40, 48, 64, 100, 112, 128, 256, 272, 400, 512, 720, 1008,
+                   1024, 1536, 2048, 2560, 3072, 4000, 4096, 5120, 6144, 8192, 10240, 12288, 14336, 16384, 65536)
 
 
 def row_sweep(workloads):
