@@ -84,6 +84,17 @@ RANDOM_CASES = [
     (9, 8, 7, 200, 2, 8, 8),
     (10, 6, 1, 500, 3, 1, 0),
     (11, 2, 200, 8, 40, 64, 0),
+    # 16-byte multiples under 1 KiB: the most whole rows in 4 KiB (48, 112,
+    # 272, 400, 720, 1008 B), tiles of whole 128-byte lines on 256 threads
+    # (688 B) and on 128 threads (832 B), each over several tiles per run
+    (12, 4, 30, 60, 2, 48, 0),
+    (13, 8, 20, 40, 3, 112, 0),
+    (14, 4, 25, 30, 1, 272, 0),
+    (15, 2, 40, 20, 4, 400, 0),
+    (16, 4, 15, 25, 0, 688, 0),
+    (17, 8, 10, 15, 2, 720, 0),
+    (18, 4, 12, 20, 1, 832, 0),
+    (19, 2, 18, 30, 3, 1008, 0),
 ]
 
 
