@@ -100,7 +100,7 @@ def test_fuzz_route_build(thd):
     # reach (a 16-row block spanning 16 one-row segments).  Runs in both orders and the split matrix must
     # equal the oracle's, and a swap of row-stamped 16-byte rows in each
     # direction must fetch the rows the oracle names.  THD_FUZZ_ROUTES sets
-    # the number of cases (default 300; a one-off run of 20000 passed).
+    # the number of cases (default 300; one-off runs of 20000 passed).
     import torch
     n_cases = int(os.environ.get("THD_FUZZ_ROUTES", "300"))
     rng = np.random.default_rng([W.BASE_SEED, 4242])
