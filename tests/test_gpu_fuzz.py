@@ -25,8 +25,11 @@ from gpu_util import CODE_OF_KIND, check_route_matches_oracle, dev_i32, dev_i64,
 
 pytestmark = pytest.mark.gpu
 
-ROW_BYTES = [1, 2, 3, 4, 6, 8, 12, 16, 20, 32, 48, 64, 100, 256, 1000, 1152, 1536, 2000, 2560, 3584, 4096, 4112,
-             10240]
+ROW_BYTES = [1, 2, 3, 4, 6, 8, 12, 16, 20, 32, 48, 64, 100, 256, 272, 400, 720, 1000, 1008, 1152, 1536, 2000, 2560,
+             3584, 4096, 4112, 10240]
+# THD_FUZZ_SCALE multiplies the case count of every sweep but the route builds
+# (THD_FUZZ_ROUTES sets that one); the first cases stay the same.
+SCALE = max(1, int(os.environ.get("THD_FUZZ_SCALE", "1")))
 CPS = [1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64]
 OFFSETS = [0, 0, 0, 1, 2, 4, 8]
 
@@ -53,7 +56,7 @@ def draw_batch(rng, cp, max_tokens):
 def test_fuzz_swap(thd):
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 900])
-    for case in range(160):
+    for case in range(160 * SCALE):
         cp = int(rng.choice(CPS))
         rb = int(rng.choice(ROW_BYTES))
         offset = int(rng.choice(OFFSETS))
@@ -133,7 +136,7 @@ def test_fuzz_swap_launch_shapes(thd):
     # the result never depends on the shape
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 930])
-    for case in range(200):
+    for case in range(200 * SCALE):
         cp = int(rng.choice(CPS[1:]))
         rb = int(rng.choice(ROW_BYTES)) if rng.random() < 0.6 else int(rng.integers(1, 9001))
         offset = int(rng.choice(OFFSETS + [3, 6, 12]))
@@ -168,7 +171,7 @@ def test_fuzz_swap_launch_shapes(thd):
 def test_fuzz_swap_batch(thd):
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 910])
-    for case in range(50):
+    for case in range(50 * SCALE):
         cp = int(rng.choice(CPS[1:]))
         docs, max_chunk, n_empty = draw_batch(rng, cp, 8000)
         w = W.random_packed([911, case], cp, docs, max_chunk, n_empty, row_shape=(1,), row_dtype="uint8")
@@ -210,7 +213,7 @@ def test_fuzz_swap_batch(thd):
 def test_fuzz_roll(thd):
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 920])
-    for case in range(60):
+    for case in range(60 * SCALE):
         cp = int(rng.choice(CPS[1:9]))
         docs, max_chunk, n_empty = draw_batch(rng, cp, 20000)
         pad_max = int(rng.integers(0, 2 * cp * max_chunk + 1))
@@ -249,7 +252,7 @@ def test_fuzz_pack(thd):
     pad, eod = 0, 1
     codes = dict(CODE_OF_KIND, PACK_DOCS=thd.THD_ERR_PACK_DOCS, PACK_CAPACITY=thd.THD_ERR_PACK_CAPACITY)
     rng = np.random.default_rng([W.BASE_SEED, 940])
-    for case in range(120):
+    for case in range(120 * SCALE):
         batch = int(rng.integers(1, 41))
         seq = int(rng.integers(1, min(5000, 40000 // batch) + 1))
         eod_rate = float(rng.choice([0.0, 0.001, 0.01, 0.05, 0.3]))
@@ -304,7 +307,7 @@ def test_fuzz_bad_boundaries(thd):
     # rule and no swap writes anything
     import torch
     rng = np.random.default_rng([W.BASE_SEED, 950])
-    for case in range(60):
+    for case in range(60 * SCALE):
         cp = int(rng.choice([2, 3, 4, 8, 16, 64, 128]))
         n_docs = int(rng.choice([3, 100, 1500, 14000]))
         max_chunk = max(1, min(8, 120000 // (2 * cp * n_docs)))
